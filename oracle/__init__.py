@@ -1,0 +1,212 @@
+"""CPU oracle for the block-scaled FP8 W8A16 GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never touches it, and this package imports nothing from
+the product.
+
+The arithmetic lives in ``w8a16_oracle.c`` (plain C, IEEE double): an exact
+OCP E4M3FN decode, an exact BF16 decode, per-output sums over 128-wide K
+blocks with the block's FP32 scale applied once to each block's partial dot
+product, and one round-to-nearest-even to BF16 straight from double.  It
+follows the page "w8a16_gemm_pipelined_m32.rs": the operand layouts in the
+doc comment of ``w8a16_gemm_pipelined_m32_strided``, the one-scale-per-K-step
+rule in the doc comment of ``W8A16_M32_K_BLOCK`` and the fold points of the
+module doc's "Numerics" paragraph.
+
+This module is argument marshalling around that C code, plus the parity
+tolerance the GPU result is graded with.
+
+Parity pins: every function here is pinned by ``tests/test_oracle.py``
+(closed-form and library witnesses for the decodes and the rounding, brute
+force with exact rationals for the GEMM, and invariants).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w8a16_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+K_BLOCK = 128
+
+
+def build(force: bool = False) -> str:
+    """Compile ``liboracle.so`` next to its source (gcc, -O2, no fast-math,
+    no FMA contraction, OpenMP over output elements)."""
+    if force or not os.path.exists(_LIB) or \
+            os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        u32 = ctypes.c_uint32
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_rne.restype = ctypes.c_uint16
+        lib.oracle_w8a16_gemm.argtypes = [u16p, u32, u8p, f32p, u16p, u32,
+                                          u32, u32, u32, f64p, f64p,
+                                          ctypes.c_int]
+        lib.oracle_w8a16_gemm.restype = ctypes.c_int
+        lib.oracle_w8a16_gemm_at.argtypes = [u16p, u32, u8p, f32p, u32, u32,
+                                             u32, u32p, u32p, ctypes.c_int64,
+                                             u16p, f64p, f64p, ctypes.c_int]
+        lib.oracle_w8a16_gemm_at.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(arr: np.ndarray, ctype):
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3FN byte (NaN for 0x7F and 0xFF)."""
+    return _load().oracle_e4m3_value(int(code) & 0xFF)
+
+
+def bf16_value(bits: int) -> float:
+    """Value of one BF16 bit pattern."""
+    return _load().oracle_bf16_value(int(bits) & 0xFFFF)
+
+
+def bf16_rne(x: float) -> int:
+    """BF16 bits nearest to the double ``x`` (ties to even), rounded once."""
+    return int(_load().oracle_bf16_rne(float(x)))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _check_operands(a, w, scale, m, n, k, a_row_stride):
+    assert a.dtype == np.uint16 and w.dtype == np.uint8 and \
+        scale.dtype == np.float32
+    assert a.flags.c_contiguous and w.flags.c_contiguous and \
+        scale.flags.c_contiguous
+    assert a.size >= (m - 1) * a_row_stride + k, "A too small for its pitch"
+    assert w.size >= n * k, "W too small"
+    assert scale.size >= ((n + K_BLOCK - 1) // K_BLOCK) * (k // K_BLOCK)
+
+
+def gemm(a: np.ndarray, w: np.ndarray, scale: np.ndarray, m: int, n: int,
+         k: int, a_row_stride: Optional[int] = None,
+         c_row_stride: Optional[int] = None, threads: int = 0,
+         c_init: Optional[np.ndarray] = None
+         ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Whole GEMM.  ``a`` holds BF16 bits (uint16) with row pitch
+    ``a_row_stride`` (default k), ``w`` E4M3 bytes [n, k], ``scale`` float32
+    [ceil(n/128), k/128].  Returns (c_bits [m, c_row_stride] uint16,
+    tot [m, n] float64, bound [m, n] float64).  Elements of C outside the
+    first n columns keep ``c_init`` (zeros by default)."""
+    a_row_stride = k if a_row_stride is None else int(a_row_stride)
+    c_row_stride = n if c_row_stride is None else int(c_row_stride)
+    a = np.ascontiguousarray(a).reshape(-1)
+    w = np.ascontiguousarray(w).reshape(-1)
+    scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+    _check_operands(a, w, scale, m, n, k, a_row_stride)
+    if c_init is None:
+        c = np.zeros((m, c_row_stride), dtype=np.uint16)
+    else:
+        c = np.array(c_init, dtype=np.uint16).reshape(m, c_row_stride).copy()
+    tot = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = _load().oracle_w8a16_gemm(
+        _ptr(a, ctypes.c_uint16), a_row_stride, _ptr(w, ctypes.c_uint8),
+        _ptr(scale, ctypes.c_float), _ptr(c, ctypes.c_uint16), c_row_stride,
+        m, n, k, _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double),
+        int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape m=%d n=%d k=%d" % (m, n, k))
+    return c, tot, bound
+
+
+def gemm_at(a: np.ndarray, w: np.ndarray, scale: np.ndarray, m: int, n: int,
+            k: int, rows: np.ndarray, cols: np.ndarray,
+            a_row_stride: Optional[int] = None, threads: int = 0
+            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Selected outputs C[rows[s], cols[s]].  Returns (c_bits uint16 [s],
+    tot float64 [s], bound float64 [s])."""
+    a_row_stride = k if a_row_stride is None else int(a_row_stride)
+    a = np.ascontiguousarray(a).reshape(-1)
+    w = np.ascontiguousarray(w).reshape(-1)
+    scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+    _check_operands(a, w, scale, m, n, k, a_row_stride)
+    rows = np.ascontiguousarray(rows, dtype=np.uint32).reshape(-1)
+    cols = np.ascontiguousarray(cols, dtype=np.uint32).reshape(-1)
+    assert rows.size == cols.size
+    ns = rows.size
+    c = np.empty(ns, dtype=np.uint16)
+    tot = np.empty(ns, dtype=np.float64)
+    bound = np.empty(ns, dtype=np.float64)
+    rc = _load().oracle_w8a16_gemm_at(
+        _ptr(a, ctypes.c_uint16), a_row_stride, _ptr(w, ctypes.c_uint8),
+        _ptr(scale, ctypes.c_float), m, n, k, _ptr(rows, ctypes.c_uint32),
+        _ptr(cols, ctypes.c_uint32), ns, _ptr(c, ctypes.c_uint16),
+        _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double),
+        int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape or sample index")
+    return c, tot, bound
+
+
+# ---------------------------------------------------------------------------
+# Parity tolerance.  A GPU result g for one output passes iff, in double,
+#     |g - oracle| <= 2^-8 * B + ulp(oracle)
+# where B = sum |a*w*s| over the output's K range and ulp(v) is the BF16
+# spacing at v: 2^(max(floor(log2|v|), -126) - 7), with ulp(0) = 2^-133.
+# A NaN or infinite GPU value fails.
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact BF16 bits -> float64 (vectorised form of bf16_value)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.where(v > 0, np.maximum(e, -126.0), -126.0)
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def within_tolerance(gpu_bits: np.ndarray, oracle_bits: np.ndarray,
+                     bound: np.ndarray) -> np.ndarray:
+    """Boolean mask: True where the GPU output passes the parity bar."""
+    g = bf16_bits_to_f64(gpu_bits)
+    o = bf16_bits_to_f64(oracle_bits)
+    lim = np.ldexp(np.asarray(bound, dtype=np.float64), -8) + bf16_ulp(o)
+    ok = np.isfinite(g) & (np.abs(g - o) <= lim)
+    return ok

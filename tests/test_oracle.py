@@ -1,0 +1,354 @@
+"""Pins for the CPU oracle (CPU only).
+
+The oracle is checked against things other than itself:
+  * library witnesses: torch's float8_e4m3fn decode and its float32->bfloat16
+    rounding (independent code);
+  * the OCP FP8 specification's anchor values (tests/golden/e4m3_anchors.txt);
+  * exact rational arithmetic (fractions.Fraction) on tiny GEMMs, rounded to
+    BF16 by a brute-force nearest search over every finite BF16 value;
+  * invariants of the block-scaled GEMM (zero weights, block-scale doubling,
+    sign symmetry, row independence, permutations of whole K blocks, a
+    permutation-matrix weight, one scaled dot product).
+"""
+
+import bisect
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+FINITE_CODES = [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def torch_e4m3(codes):
+    t = torch.tensor(list(codes), dtype=torch.uint8).view(torch.float8_e4m3fn)
+    return t.float().double().tolist()
+
+
+def torch_bf16_bits(x32):
+    t = torch.from_numpy(np.asarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------- E4M3
+
+def test_e4m3_matches_torch_on_all_finite_codes():
+    ref = torch_e4m3(FINITE_CODES)
+    got = [oracle.e4m3_value(c) for c in FINITE_CODES]
+    for c, r, g in zip(FINITE_CODES, ref, got):
+        assert math.copysign(1.0, r) == math.copysign(1.0, g), hex(c)
+        assert r == g, (hex(c), r, g)
+
+
+def test_e4m3_nan_codes():
+    assert math.isnan(oracle.e4m3_value(0x7F))
+    assert math.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_spec_anchors():
+    # tests/golden/e4m3_anchors.txt: code -> value pairs taken from the OCP
+    # 8-bit floating point specification (OFP8), E4M3 column.
+    path = os.path.join(GOLDEN, "e4m3_anchors.txt")
+    n = 0
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            code, value = line.split()
+            got = oracle.e4m3_value(int(code, 16))
+            assert got == float(Fraction(value)), (code, value, got)
+            n += 1
+    assert n >= 10
+
+
+def test_e4m3_order_and_symmetry():
+    pos = [oracle.e4m3_value(c) for c in range(0x00, 0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:])), "codes 0..0x7E increase"
+    for c in range(0x00, 0x7F):
+        assert oracle.e4m3_value(c | 0x80) == -oracle.e4m3_value(c)
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) == -1.0
+    # 126 distinct positive values plus zero; every one is a BF16 value.
+    assert len(set(pos)) == 127
+    for v in pos:
+        assert oracle.bf16_value(oracle.bf16_rne(v)) == v
+
+
+# --------------------------------------------------------------------- BF16
+
+def test_bf16_value_is_top_half_of_float32():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 16, 4000, dtype=np.uint32).astype(np.uint16)
+    for b in bits[:500]:
+        f = np.array([np.uint32(b) << np.uint32(16)], np.uint32).view(np.float32)[0]
+        v = oracle.bf16_value(int(b))
+        if np.isnan(f):
+            assert math.isnan(v)
+        else:
+            assert v == float(f)
+
+
+def test_bf16_rne_matches_torch_on_float_inputs():
+    rng = np.random.default_rng(6)
+    xs = np.concatenate([
+        rng.standard_normal(3000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-38).astype(np.float32),   # subnormals
+        (rng.standard_normal(500) * 1e-44).astype(np.float32),
+        # exact BF16 midpoints (ties) in several binades
+        (np.arange(1, 500, dtype=np.float32) * 2.0 + 1.0) * np.float32(2.0 ** -9),
+        np.float32([3.3895314e38, -3.3895314e38, 3.4e38, 1.17549435e-38]),
+    ]).astype(np.float32)
+    ref = torch_bf16_bits(xs)
+    got = np.array([oracle.bf16_rne(float(x)) for x in xs], dtype=np.uint16)
+    assert np.array_equal(ref, got)
+
+
+def test_bf16_rne_constructed_cases():
+    assert oracle.bf16_rne(1 + 2 ** -8) == 0x3F80          # tie -> even (down)
+    assert oracle.bf16_rne(1 + 3 * 2 ** -8) == 0x3F82      # tie -> even (up)
+    # the double-rounding trap: via float this would become 1.0
+    assert oracle.bf16_rne(1 + 2 ** -8 + 2 ** -40) == 0x3F81
+    assert oracle.bf16_rne(-(1 + 2 ** -8 + 2 ** -40)) == 0xBF81
+    assert oracle.bf16_rne(0.0) == 0x0000
+    assert oracle.bf16_rne(-0.0) == 0x8000
+    assert oracle.bf16_rne(2.0 ** -133) == 0x0001          # smallest subnormal
+    assert oracle.bf16_rne(2.0 ** -134) == 0x0000          # tie to even zero
+    assert oracle.bf16_rne(3 * 2.0 ** -134) == 0x0002
+    maxf = (2 - 2 ** -7) * 2.0 ** 127
+    assert oracle.bf16_rne(maxf) == 0x7F7F
+    assert oracle.bf16_rne((2 - 2 ** -8) * 2.0 ** 127) == 0x7F80  # midpoint -> inf
+    assert oracle.bf16_rne(-(2 - 2 ** -8 - 2 ** -30) * 2.0 ** 127) == 0xFF7F
+    assert oracle.bf16_rne(float("inf")) == 0x7F80
+    assert oracle.bf16_rne(float("nan")) & 0x7FC0 == 0x7FC0
+
+
+# ------------------------------------------------- brute force with rationals
+
+_BF16_POS = None
+
+
+def _bf16_positive_table():
+    """Every finite positive BF16 value, as (Fraction, bits), ascending."""
+    global _BF16_POS
+    if _BF16_POS is None:
+        bits = np.arange(1, 0x7F80, dtype=np.uint32)
+        vals = (bits << 16).astype(np.uint32).view(np.float32)
+        _BF16_POS = ([Fraction(float(v)) for v in vals], bits.tolist())
+    return _BF16_POS
+
+
+def brute_bf16_rne(x: Fraction) -> int:
+    """Nearest BF16 to an exact rational, ties to the even bit pattern,
+    found by search over the sorted list of all finite BF16 values."""
+    if x == 0:
+        return 0
+    vals, bits = _bf16_positive_table()
+    sign = 0x8000 if x < 0 else 0
+    a = abs(x)
+    maxv = vals[-1]
+    half_ulp_max = Fraction(2) ** 119          # half the spacing at the top
+    if a >= maxv + half_ulp_max:
+        return sign | 0x7F80
+    i = bisect.bisect_left(vals, a)
+    cands = []
+    if i < len(vals):
+        cands.append((vals[i], bits[i]))
+    if i > 0:
+        cands.append((vals[i - 1], bits[i - 1]))
+    else:
+        cands.append((Fraction(0), 0))
+    best = min(cands, key=lambda vb: (abs(vb[0] - a), vb[1] & 1))
+    return sign | best[1]
+
+
+def _rand_codes(rng, shape):
+    return rng.choice(np.array(FINITE_CODES, dtype=np.uint8), size=shape)
+
+
+def _exact_gemm(a_bits, a_stride, w_codes, scale, m, n, k):
+    """Exact rational C (list of lists) and the bound; written from the
+    definition with torch as the E4M3 decoder."""
+    wv = np.array(torch_e4m3(w_codes.reshape(-1).tolist())).reshape(n, k)
+    av = (a_bits.reshape(-1).astype(np.uint32) << 16).view(np.float32)
+    kb = k // 128
+    out = []
+    for i in range(m):
+        row = []
+        for j in range(n):
+            tot = Fraction(0)
+            for b in range(kb):
+                p = Fraction(0)
+                for t in range(128):
+                    kk = 128 * b + t
+                    p += Fraction(float(av[i * a_stride + kk])) * Fraction(float(wv[j, kk]))
+                tot += Fraction(float(scale[j // 128, b])) * p
+            row.append(tot)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("m,n,k,a_pad", [(1, 1, 128, 0), (2, 5, 256, 8),
+                                          (3, 130, 128, 16), (1, 129, 256, 0)])
+def test_gemm_equals_exact_rational_then_rne(m, n, k, a_pad):
+    rng = np.random.default_rng(100 + m * 1000 + n + k)
+    a_stride = k + a_pad
+    a = np.full((m, a_stride), datagen.A_PAD_BITS, dtype=np.uint16)
+    af = rng.standard_normal((m, k)).astype(np.float32)
+    af[:, ::17] *= np.float32(2.0 ** -60)        # tiny activations
+    af[:, 5::31] *= np.float32(2.0 ** 40)        # huge activations
+    a[:, :k] = torch_bf16_bits(af)
+    w = _rand_codes(rng, (n, k))
+    nb = (n + 127) // 128
+    scale = np.exp2(rng.uniform(-20, 5, size=(nb, k // 128))).astype(np.float32)
+    scale[0, 0] = np.float32(0.75)               # not a power of two
+    c, tot, bound = oracle.gemm(a, w, scale, m, n, k, a_row_stride=a_stride)
+    exact = _exact_gemm(a, a_stride, w, scale, m, n, k)
+    skipped = 0
+    for i in range(m):
+        for j in range(n):
+            x = exact[i][j]
+            # the double total differs from the exact one by rounding only
+            assert abs(Fraction(tot[i, j]) - x) <= Fraction(bound[i, j]) * Fraction(2) ** -48
+            want = brute_bf16_rne(x)
+            if want != c[i, j]:
+                # only acceptable when the exact value sits on a rounding
+                # boundary closer than the double total can resolve
+                lo = Fraction(oracle.bf16_value(int(want)))
+                hi = Fraction(oracle.bf16_value(int(c[i, j])))
+                mid = (lo + hi) / 2
+                assert abs(x - mid) <= Fraction(bound[i, j]) * Fraction(2) ** -48, (i, j)
+                skipped += 1
+    assert skipped <= 1
+
+
+def test_c_pitch_and_pad_untouched():
+    p = datagen.make_problem(3, 130, 256, seed=7, a_row_stride=264,
+                             c_row_stride=141, c_extra_rows=0)
+    init = np.full((3, 141), 0xFFFF, dtype=np.uint16)
+    c, _, _ = oracle.gemm(p.a, p.w, p.scale, 3, 130, 256, a_row_stride=264,
+                          c_row_stride=141, c_init=init)
+    assert (c[:, 130:] == 0xFFFF).all()
+    c2, _, _ = oracle.gemm(np.ascontiguousarray(p.a[:, :256]), p.w, p.scale,
+                           3, 130, 256)
+    assert np.array_equal(c[:, :130], c2)
+
+
+def test_gemm_at_matches_full():
+    p = datagen.make_problem(4, 300, 384, seed=8)
+    c, tot, bound = oracle.gemm(p.a, p.w, p.scale, 4, 300, 384)
+    rows, cols = datagen.sample_indices(4, 300, 50, seed=1)
+    cs, ts, bs = oracle.gemm_at(p.a, p.w, p.scale, 4, 300, 384, rows, cols)
+    assert np.array_equal(cs, c[rows, cols])
+    assert np.array_equal(ts, tot[rows, cols])
+    assert np.array_equal(bs, bound[rows, cols])
+
+
+def test_rejects_invalid_shapes():
+    a = np.zeros(256, np.uint16)
+    w = np.zeros(256, np.uint8)
+    s = np.zeros(2, np.float32)
+    with pytest.raises(ValueError):
+        oracle.gemm(a, w, s, 1, 1, 200)
+
+
+# --------------------------------------------------------------- invariants
+
+def _prob(m=3, n=256, k=512, seed=11):
+    return datagen.make_problem(m, n, k, seed)
+
+
+def test_zero_weights_give_zero():
+    p = _prob()
+    c, tot, _ = oracle.gemm(p.a, np.zeros_like(p.w), p.scale, p.m, p.n, p.k)
+    assert (tot == 0).all()
+    assert ((c == 0) | (c == 0x8000)).all()
+
+
+def test_doubling_one_block_scale_adds_that_block():
+    p = _prob()
+    _, tot0, bnd = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k)
+    nb, kb = 1, 2
+    s2 = p.scale.copy()
+    s2[nb, kb] *= 2
+    _, tot1, _ = oracle.gemm(p.a, p.w, s2, p.m, p.n, p.k)
+    # the block's own contribution, from a separate call with only that block
+    w_only = np.zeros_like(p.w)
+    w_only[128 * nb:128 * (nb + 1), 128 * kb:128 * (kb + 1)] = \
+        p.w[128 * nb:128 * (nb + 1), 128 * kb:128 * (kb + 1)]
+    _, tblk, _ = oracle.gemm(p.a, w_only, p.scale, p.m, p.n, p.k)
+    diff = tot1 - tot0
+    assert np.all(np.abs(diff - tblk) <= bnd * 2.0 ** -48)
+    others = np.ones(p.n, bool)
+    others[128 * nb:128 * (nb + 1)] = False
+    assert np.array_equal(tot1[:, others], tot0[:, others])
+
+
+def test_negating_a_negates_c():
+    p = _prob()
+    c0, _, _ = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k)
+    c1, _, _ = oracle.gemm(p.a ^ np.uint16(0x8000), p.w, p.scale, p.m, p.n, p.k)
+    assert np.array_equal(c1, c0 ^ np.uint16(0x8000))
+
+
+def test_rows_are_independent():
+    p = _prob(m=4)
+    c0, _, _ = oracle.gemm(p.a, p.w, p.scale, 4, p.n, p.k)
+    for i in range(4):
+        ci, _, _ = oracle.gemm(np.ascontiguousarray(p.a[i]), p.w, p.scale, 1, p.n, p.k)
+        assert np.array_equal(ci[0], c0[i])
+
+
+def test_permuting_k_blocks_with_scales():
+    p = _prob(k=512)
+    perm = [2, 0, 3, 1]
+    cols = np.concatenate([np.arange(128 * b, 128 * (b + 1)) for b in perm])
+    a2 = np.ascontiguousarray(p.a[:, cols])
+    w2 = np.ascontiguousarray(p.w[:, cols])
+    s2 = np.ascontiguousarray(p.scale[:, perm])
+    _, t0, bnd = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k)
+    _, t1, _ = oracle.gemm(a2, w2, s2, p.m, p.n, p.k)
+    assert np.all(np.abs(t1 - t0) <= bnd * 2.0 ** -48)
+
+
+def test_permutation_matrix_weight_selects_columns():
+    m, n, k = 5, 256, 256
+    rng = np.random.default_rng(12)
+    pi = rng.permutation(k)
+    w = np.zeros((n, k), np.uint8)
+    w[np.arange(n), pi] = 0x38                    # E4M3 1.0
+    scale = np.ones((2, 2), np.float32)
+    a = torch_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    c, _, _ = oracle.gemm(a, w, scale, m, n, k)
+    assert np.array_equal(c, a[:, pi])
+
+
+def test_single_block_is_scaled_dot_product():
+    rng = np.random.default_rng(13)
+    a = torch_bf16_bits(rng.standard_normal((1, 128)).astype(np.float32))
+    w = _rand_codes(rng, (1, 128))
+    s = np.array([[0.3]], np.float32)
+    _, tot, _ = oracle.gemm(a, w, s, 1, 1, 128)
+    av = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[0]
+    wv = np.array(torch_e4m3(w[0].tolist()))
+    ref = float(np.float32(0.3)) * float(np.dot(av, wv))
+    assert abs(tot[0, 0] - ref) <= 2.0 ** -45 * float(np.abs(av * wv).sum())
+
+
+def test_golden_regression_small_workload():
+    """Stored output of the smallest workload, written by
+    tests/golden/make_golden.py from the oracle alone; guards against
+    unintended changes to the oracle's arithmetic."""
+    path = os.path.join(GOLDEN, "m1_n256_k256.c_bits.txt")
+    want = np.loadtxt(path, dtype=np.int64).astype(np.uint16)
+    p = datagen.make_workload(datagen.workload("m1_n256_k256"))
+    c, _, _ = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k)
+    assert np.array_equal(c.reshape(-1), want.reshape(-1))
