@@ -1,0 +1,178 @@
+"""Block-scaled FP8 W8A16 small-M GEMM for MI355X (gfx950).
+
+Thin binding over ``libw8a16.so`` (the C ABI in ``include/w8a16.h``):
+argument marshalling only.  Every step of the GEMM runs in the library's
+HIP kernels; PyTorch supplies device memory and the current stream.  If the
+library has not been built, every call raises -- there is no fallback.
+
+    C[i, j] = bf16( sum_b S[j//128, b] * sum_t A[i, 128b+t] * W[j, 128b+t] )
+
+A is BF16 [m, k] (any row pitch that is a multiple of 8), W is FP8 E4M3
+[n, k] (torch.float8_e4m3fn or its uint8 bytes), S is float32
+[ceil(n/128), k/128], C is BF16 [m, n] (any row pitch >= n).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a16.so")
+
+OK = 0
+ERR_M_ZERO = 1
+ERR_K_NOT_MULT_128 = 2
+ERR_PITCH_TOO_SHORT = 3
+ERR_A_STRIDE_ALIGN = 4
+ERR_N_ZERO = 5
+ERR_NULL_PTR = 6
+ERR_BAD_PLAN = 7
+ERR_HIP = 8
+
+KERNEL_STREAM = 1
+KERNEL_TILE = 2
+
+# Symbols the C ABI exports (include/w8a16.h).
+EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
+           "w8a16_gemm_planned", "w8a16_status_string", "w8a16_last_error")
+
+
+class W8A16Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("w8a16 status %d: %s" % (status, message))
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_uint32), ("m_blocks", ctypes.c_uint32),
+                ("n_blocks", ctypes.c_uint32), ("splits", ctypes.c_uint32),
+                ("steps_per_split", ctypes.c_uint32), ("m_tiles", ctypes.c_uint32),
+                ("n_tiles", ctypes.c_uint32), ("grid", ctypes.c_uint32),
+                ("block", ctypes.c_uint32), ("lds_bytes", ctypes.c_uint32),
+                ("workspace_bytes", ctypes.c_uint64),
+                ("counter_count", ctypes.c_uint32), ("cu_count", ctypes.c_uint32)]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libw8a16.so (raises if it is missing: build it first with
+    ``python -m block_scaled_fp8_w8a16_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libw8a16.so is not built (%s); run "
+                              "python -m block_scaled_fp8_w8a16_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        u32, vp = ctypes.c_uint32, ctypes.c_void_p
+        lib.w8a16_check_args.argtypes = [u32] * 5
+        lib.w8a16_check_args.restype = ctypes.c_int
+        lib.w8a16_plan.argtypes = [u32, u32, u32, u32, ctypes.POINTER(Plan)]
+        lib.w8a16_plan.restype = ctypes.c_int
+        lib.w8a16_plan_finalize.argtypes = [u32, u32, u32, ctypes.POINTER(Plan)]
+        lib.w8a16_plan_finalize.restype = ctypes.c_int
+        lib.w8a16_gemm.argtypes = [vp, u32, vp, vp, vp, u32, u32, u32, u32, vp]
+        lib.w8a16_gemm.restype = ctypes.c_int
+        lib.w8a16_gemm_planned.argtypes = [vp, u32, vp, vp, vp, u32, u32, u32, u32,
+                                           ctypes.POINTER(Plan), vp]
+        lib.w8a16_gemm_planned.restype = ctypes.c_int
+        lib.w8a16_status_string.argtypes = [ctypes.c_int]
+        lib.w8a16_status_string.restype = ctypes.c_char_p
+        lib.w8a16_last_error.argtypes = []
+        lib.w8a16_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().w8a16_last_error().decode()
+
+
+def status_string(status: int) -> str:
+    return library().w8a16_status_string(int(status)).decode()
+
+
+def _raise_if(status: int):
+    if status != OK:
+        raise W8A16Error(status, last_error() or status_string(status))
+
+
+def check_args(m: int, n: int, k: int, a_row_stride: int, c_row_stride: int) -> int:
+    """Status of the scalar argument checks (no GPU call)."""
+    return int(library().w8a16_check_args(m, n, k, a_row_stride, c_row_stride))
+
+
+def plan(m: int, n: int, k: int, cu_count: int = 0) -> Plan:
+    """Default launch plan (no GPU call)."""
+    p = Plan()
+    _raise_if(library().w8a16_plan(m, n, k, cu_count, ctypes.byref(p)))
+    return p
+
+
+def make_plan(m: int, n: int, k: int, kernel: int, m_blocks: int, n_blocks: int,
+              splits: int, cu_count: int = 0) -> Plan:
+    """A caller-chosen plan, checked and completed by the library."""
+    p = Plan()
+    p.kernel, p.m_blocks, p.n_blocks, p.splits, p.cu_count = \
+        kernel, m_blocks, n_blocks, splits, cu_count
+    _raise_if(library().w8a16_plan_finalize(m, n, k, ctypes.byref(p)))
+    return p
+
+
+def gemm_raw(a_ptr: int, a_row_stride: int, w_ptr: int, scale_ptr: int, c_ptr: int,
+             c_row_stride: int, m: int, n: int, k: int, stream: int = 0,
+             plan_: Optional[Plan] = None) -> int:
+    """Direct call of the C ABI with device addresses; returns the status."""
+    lib = library()
+    if plan_ is None:
+        return int(lib.w8a16_gemm(a_ptr, a_row_stride, w_ptr, scale_ptr, c_ptr,
+                                  c_row_stride, m, n, k, stream))
+    return int(lib.w8a16_gemm_planned(a_ptr, a_row_stride, w_ptr, scale_ptr, c_ptr,
+                                      c_row_stride, m, n, k, ctypes.byref(plan_),
+                                      stream))
+
+
+def gemm(a, w, scale, c=None, *, plan_: Optional[Plan] = None, stream=None):
+    """C = A @ dequant(W)^T on the current (or given) torch stream.
+
+    a: bfloat16 [m, k] CUDA tensor, unit column stride, row stride a multiple
+    of 8.  w: float8_e4m3fn or uint8 [n, k] contiguous.  scale: float32
+    [ceil(n/128), k/128] contiguous.  c: optional bfloat16 [m, n] output with
+    unit column stride (a new contiguous tensor if None).  Returns c."""
+    import torch
+    if a.dim() != 2 or w.dim() != 2:
+        raise ValueError("a and w must be 2-D")
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("w must be [n, k] with the k of a")
+    if a.dtype != torch.bfloat16 or a.stride(1) != 1:
+        raise ValueError("a must be bfloat16 with unit column stride")
+    if w.dtype not in (torch.uint8, torch.float8_e4m3fn) or not w.is_contiguous():
+        raise ValueError("w must be contiguous float8_e4m3fn or uint8")
+    if scale.dtype != torch.float32 or not scale.is_contiguous():
+        raise ValueError("scale must be contiguous float32")
+    nb = (n + 127) // 128
+    if scale.numel() < nb * (k // 128 if k % 128 == 0 else 0):
+        raise ValueError("scale must hold [ceil(n/128), k/128] values")
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    if c.dtype != torch.bfloat16 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+        raise ValueError("c must be bfloat16 [m, n] with unit column stride")
+    for t in (a, w, scale, c):
+        if not t.is_cuda:
+            raise ValueError("all operands must be GPU tensors")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    a_rs = a.stride(0) if m > 1 else max(a.stride(0), k)
+    c_rs = c.stride(0) if m > 1 else max(c.stride(0), n)
+    st = gemm_raw(a.data_ptr(), a_rs, w.data_ptr(), scale.data_ptr(), c.data_ptr(),
+                  c_rs, m, n, k, stream.cuda_stream, plan_)
+    _raise_if(st)
+    return c

@@ -1,0 +1,57 @@
+"""Build ``libw8a16.so`` (the HIP kernels and their C ABI) for gfx950.
+
+Run as ``python -m block_scaled_fp8_w8a16_amd.build``.  The library is built
+in-tree next to this file so it travels with the source tree.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libw8a16.so")
+
+SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_kernel.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Packed FP32 ops (v_pk_*_f32) are kept out of the device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    objs = []
+    builddir = os.path.join(HERE, "_build")
+    os.makedirs(builddir, exist_ok=True)
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(builddir, src + ".o")
+        if src.endswith(".hip"):
+            cmd = [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+                   "-Wall", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS + \
+                  ["-c", path, "-o", obj]
+        else:
+            cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+                   "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

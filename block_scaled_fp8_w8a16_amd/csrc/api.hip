@@ -1,0 +1,205 @@
+// C ABI of the W8A16 GEMM: argument checks, plan, workspace, launch.
+//
+// The entry point mirrors `w8a16_gemm_pipelined_m32_strided` on the page
+// "w8a16_gemm_pipelined_m32.rs": the same operands and strides, the same
+// rejections in the same order, and an asynchronous launch on the caller's
+// stream with no synchronisation.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "kernels.h"
+#include "plan.h"
+
+namespace w8a16 {
+
+namespace {
+
+// Split-K workspace and arrival counters of one (device, stream).  The
+// counters are zeroed once at allocation; every kernel that uses them
+// leaves them at zero again.
+struct Workspace {
+    float *ws = nullptr;
+    uint64_t ws_bytes = 0;
+    uint32_t *counters = nullptr;
+    uint32_t counter_count = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+std::mutex g_cu_mutex;
+std::map<int, uint32_t> g_cu_count;
+
+int hip_fail(hipError_t e, const char *what)
+{
+    char buf[256];
+    snprintf(buf, sizeof buf, "w8a16_gemm: %s failed: %s", what, hipGetErrorString(e));
+    return fail(W8A16_ERR_HIP, buf);
+}
+
+int device_cu_count(int dev, uint32_t *out)
+{
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    auto it = g_cu_count.find(dev);
+    if (it != g_cu_count.end()) {
+        *out = it->second;
+        return W8A16_OK;
+    }
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceGetAttribute");
+    g_cu_count[dev] = (uint32_t)cus;
+    *out = (uint32_t)cus;
+    return W8A16_OK;
+}
+
+// Workspace for `plan` on (dev, stream), grown if needed.  Growing waits for
+// the stream so that no earlier call still uses the old buffers.
+int get_workspace(int dev, hipStream_t stream, const w8a16_plan_t &plan, Workspace *out)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    hipError_t e;
+    if (plan.workspace_bytes > w.ws_bytes || plan.counter_count > w.counter_count) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamSynchronize");
+    }
+    if (plan.workspace_bytes > w.ws_bytes) {
+        if (w.ws)
+            (void)hipFree(w.ws);
+        w.ws = nullptr;
+        w.ws_bytes = 0;
+        e = hipMalloc(reinterpret_cast<void **>(&w.ws), plan.workspace_bytes);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMalloc(workspace)");
+        w.ws_bytes = plan.workspace_bytes;
+    }
+    if (plan.counter_count > w.counter_count) {
+        if (w.counters)
+            (void)hipFree(w.counters);
+        w.counters = nullptr;
+        w.counter_count = 0;
+        e = hipMalloc(reinterpret_cast<void **>(&w.counters),
+                      (size_t)plan.counter_count * sizeof(uint32_t));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMalloc(counters)");
+        e = hipMemsetAsync(w.counters, 0, (size_t)plan.counter_count * sizeof(uint32_t),
+                           stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMemsetAsync(counters)");
+        w.counter_count = plan.counter_count;
+    }
+    *out = w;
+    return W8A16_OK;
+}
+
+int check_call(const void *a, uint32_t a_row_stride, const void *w_fp8,
+               const float *block_scale, void *c, uint32_t c_row_stride, uint32_t m,
+               uint32_t n, uint32_t k)
+{
+    int st = check_args(m, n, k, a_row_stride, c_row_stride);
+    if (st != W8A16_OK)
+        return st;
+    if (!a || !w_fp8 || !block_scale || !c)
+        return fail(W8A16_ERR_NULL_PTR,
+                    "w8a16_gemm: a, w_fp8, block_scale and c must be non-null");
+    return W8A16_OK;
+}
+
+int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *block_scale,
+        void *c, uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
+        const w8a16_plan_t &plan, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    Workspace wsp;
+    if (plan.splits > 1) {
+        int st = get_workspace(dev, stream, plan, &wsp);
+        if (st != W8A16_OK)
+            return st;
+    }
+    GemmArgs g;
+    g.a = static_cast<const uint8_t *>(a);
+    g.w = static_cast<const uint8_t *>(w_fp8);
+    g.scale = block_scale;
+    g.c = static_cast<uint8_t *>(c);
+    g.ws = wsp.ws;
+    g.counters = wsp.counters;
+    g.a_stride = a_row_stride;
+    g.c_stride = c_row_stride;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.m_tiles = plan.m_tiles;
+    g.n_tiles = plan.n_tiles;
+    g.splits = plan.splits;
+    g.steps_per_split = plan.steps_per_split;
+    if (plan.kernel == W8A16_KERNEL_STREAM)
+        e = launch_stream(g, plan, stream);
+    else
+        e = launch_tile(g, plan, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    set_last_error("");
+    return W8A16_OK;
+}
+
+}  // namespace
+
+}  // namespace w8a16
+
+extern "C" {
+
+int w8a16_gemm(const void *a, uint32_t a_row_stride, const void *w_fp8,
+               const float *block_scale, void *c, uint32_t c_row_stride, uint32_t m,
+               uint32_t n, uint32_t k, void *stream)
+{
+    using namespace w8a16;
+    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    if (st != W8A16_OK)
+        return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    uint32_t cus = 0;
+    st = device_cu_count(dev, &cus);
+    if (st != W8A16_OK)
+        return st;
+    w8a16_plan_t plan;
+    st = make_plan(m, n, k, cus, &plan);
+    if (st != W8A16_OK)
+        return st;
+    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan,
+               static_cast<hipStream_t>(stream));
+}
+
+int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
+                       const float *block_scale, void *c, uint32_t c_row_stride,
+                       uint32_t m, uint32_t n, uint32_t k, const w8a16_plan_t *plan,
+                       void *stream)
+{
+    using namespace w8a16;
+    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    if (st != W8A16_OK)
+        return st;
+    if (!plan)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_gemm_planned: null plan");
+    w8a16_plan_t p = *plan;
+    st = plan_finalize(m, n, k, &p);
+    if (st != W8A16_OK)
+        return st;
+    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, p,
+               static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

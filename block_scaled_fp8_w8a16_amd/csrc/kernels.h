@@ -1,0 +1,29 @@
+// Kernel launch interface shared by the C ABI and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w8a16.h"
+
+namespace w8a16 {
+
+constexpr uint32_t kWavesPerGroup = 4;
+
+// Arguments every kernel takes (by value).  Pointers are device pointers;
+// strides are in elements.
+struct GemmArgs {
+    const uint8_t *a;       // BF16 [m, a_stride]
+    const uint8_t *w;       // E4M3 [n, k]
+    const float *scale;     // FP32 [ceil(n/128), k/128]
+    uint8_t *c;             // BF16 [m, c_stride]
+    float *ws;              // split-K partial tiles (splits > 1)
+    uint32_t *counters;     // split-K arrival counters, zero between calls
+    uint32_t a_stride, c_stride, m, n, k;
+    uint32_t m_tiles, n_tiles, splits, steps_per_split;
+};
+
+hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+
+}  // namespace w8a16

@@ -1,0 +1,244 @@
+// Argument checks, launch planning and status text for the W8A16 GEMM.
+//
+// Pure host code with no HIP dependency, so the checks and the plans can be
+// graded on a machine without a GPU.
+//
+// The argument rules are those of `w8a16_gemm_pipelined_m32_strided` on the
+// page "w8a16_gemm_pipelined_m32.rs" (its `ensure!` checks, in their order):
+// m >= 1; k a positive multiple of 128 (one FP8 scale block per K step);
+// both pitches covering the used extents; a_row_stride a multiple of 8 so
+// A rows stay 16-byte aligned.  n == 0 and null pointers are rejected after
+// those, which the page does not check.
+//
+// The tile rule keeps the page's idea (small m streams the weight once,
+// large m uses a big row tile; `w8a16_pipelined_prefers_m32`,
+// `w8a16_pipelined_prefers_m64`, `w8a16_gemm_pipelined_by_m`), re-derived
+// for MI355X: 256 CUs, 64-wide waves, 16x16x32 BF16 MFMA.
+
+#include "plan.h"
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace w8a16 {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_last_error(const char *fmt_msg) { g_last_error = fmt_msg ? fmt_msg : ""; }
+
+const char *last_error() { return g_last_error.c_str(); }
+
+int fail(int status, const char *msg)
+{
+    set_last_error(msg);
+    return status;
+}
+
+int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
+               uint32_t c_row_stride)
+{
+    char buf[256];
+    if (m < 1)
+        return fail(W8A16_ERR_M_ZERO, "w8a16_gemm: m=0 has no rows to compute");
+    if (k < kKStep || k % kKStep != 0) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm: K=%u must be a positive multiple of %u (one FP8 "
+                 "scale block per K-step)", k, kKStep);
+        return fail(W8A16_ERR_K_NOT_MULT_128, buf);
+    }
+    if (a_row_stride < k || c_row_stride < n) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm: row pitches (a=%u, c=%u) must cover the used "
+                 "extents (k=%u, n=%u)", a_row_stride, c_row_stride, k, n);
+        return fail(W8A16_ERR_PITCH_TOO_SHORT, buf);
+    }
+    if (a_row_stride % 8 != 0) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm: a_row_stride=%u must keep rows 16B-aligned "
+                 "(multiple of 8 elements)", a_row_stride);
+        return fail(W8A16_ERR_A_STRIDE_ALIGN, buf);
+    }
+    if (n < 1)
+        return fail(W8A16_ERR_N_ZERO, "w8a16_gemm: n=0 has no columns to compute");
+    return W8A16_OK;
+}
+
+static uint32_t div_up(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+static bool stream_shape_supported(uint32_t mb, uint32_t nb)
+{
+    bool mb_ok = mb == 1 || mb == 2 || mb == 4;
+    bool nb_ok = nb == 1 || nb == 2 || nb == 4 || nb == 8;
+    return mb_ok && nb_ok && mb * nb <= 16;
+}
+
+static bool tile_shape_supported(uint32_t mb, uint32_t nb)
+{
+    return mb == 8 && (nb == 8 || nb == 16);
+}
+
+int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
+{
+    char buf[256];
+    if (!p)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_plan: null plan");
+    int st = check_args(m, n, k, k, n);
+    if (st != W8A16_OK)
+        return st;
+    const uint32_t ksteps = k / kKStep;
+    if (p->cu_count == 0)
+        p->cu_count = kDefaultCUs;
+    if (p->kernel == W8A16_KERNEL_STREAM) {
+        if (!stream_shape_supported(p->m_blocks, p->n_blocks)) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: stream kernel has no (m_blocks=%u, n_blocks=%u) "
+                     "variant", p->m_blocks, p->n_blocks);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->block = kWaves * 64;
+        uint32_t per_wave = p->n_blocks * kWBlockBytes + p->m_blocks * kABlockBytes;
+        uint32_t staging = kWaves * per_wave;
+        uint32_t reduce = kWaves * p->n_blocks * p->m_blocks * kAccBytes;
+        p->lds_bytes = staging > reduce ? staging : reduce;
+    } else if (p->kernel == W8A16_KERNEL_TILE && kTileKernelBuilt) {
+        if (!tile_shape_supported(p->m_blocks, p->n_blocks)) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: tile kernel has no (m_blocks=%u, n_blocks=%u) "
+                     "variant", p->m_blocks, p->n_blocks);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->block = kTileThreads;
+        p->lds_bytes = tile_lds_bytes(p->n_blocks);
+    } else {
+        snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    if (p->splits < 1 || p->splits > ksteps) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_plan: splits=%u must be in 1..%u (K steps)", p->splits, ksteps);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    // Equal step counts per split; the count of splits actually needed may
+    // shrink (e.g. 32 steps in 5 splits of 7 -> 5 splits, the last with 4).
+    p->steps_per_split = div_up(ksteps, p->splits);
+    p->splits = div_up(ksteps, p->steps_per_split);
+    p->m_tiles = div_up(m, 16 * p->m_blocks);
+    p->n_tiles = div_up(n, 16 * p->n_blocks);
+    uint64_t tiles = (uint64_t)p->m_tiles * p->n_tiles;
+    uint64_t grid = tiles * p->splits;
+    if (grid > 0x7fffffffull) {
+        snprintf(buf, sizeof buf, "w8a16_plan: grid of %llu workgroups is too large",
+                 (unsigned long long)grid);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    p->grid = (uint32_t)grid;
+    if (p->splits > 1) {
+        p->workspace_bytes = grid * (uint64_t)p->m_blocks * p->n_blocks * kAccBytes;
+        p->counter_count = (uint32_t)tiles;
+    } else {
+        p->workspace_bytes = 0;
+        p->counter_count = 0;
+    }
+    return W8A16_OK;
+}
+
+int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    if (!out)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_plan: null plan");
+    int st = check_args(m, n, k, k, n);
+    if (st != W8A16_OK)
+        return st;
+    w8a16_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.cu_count = cu_count ? cu_count : kDefaultCUs;
+    const uint32_t ksteps = k / kKStep;
+    const uint32_t nb16 = div_up(n, 16);
+    const uint32_t target = 2 * p.cu_count;   // workgroups wanted in flight
+
+    if (m > 64 && kTileKernelBuilt) {
+        // Large m: 128-row tiles with the dequantized weight tile shared by
+        // all rows; split K only if the tiles alone cannot fill the chip.
+        p.kernel = W8A16_KERNEL_TILE;
+        p.m_blocks = 8;
+        p.n_blocks = 16;
+        uint32_t tiles = div_up(m, 128) * div_up(n, 256);
+        p.splits = 1;
+        while (tiles * p.splits < p.cu_count && ksteps / (p.splits * 2) >= 8)
+            p.splits *= 2;
+    } else {
+        p.kernel = W8A16_KERNEL_STREAM;
+        p.m_blocks = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+        const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
+        // Widest column tile that still gives every CU a workgroup; the
+        // weight is read once whatever the tile, wider tiles only cut the
+        // re-reads of A.
+        uint32_t nbw = 1;
+        const uint32_t cands[3] = {4, 2, 1};
+        for (uint32_t c : cands) {
+            if (p.m_blocks * c > 16)
+                continue;
+            if (div_up(nb16, c) * m_tiles >= p.cu_count) {
+                nbw = c;
+                break;
+            }
+        }
+        p.n_blocks = nbw;
+        uint32_t tiles = div_up(nb16, nbw) * m_tiles;
+        // Split K until there are `target` workgroups, keeping at least one
+        // K step per wave in every split.
+        p.splits = 1;
+        while (tiles * p.splits < target && ksteps / (p.splits * 2) >= kWaves)
+            p.splits *= 2;
+    }
+    st = plan_finalize(m, n, k, &p);
+    if (st != W8A16_OK)
+        return st;
+    *out = p;
+    return W8A16_OK;
+}
+
+const char *status_string(int status)
+{
+    switch (status) {
+    case W8A16_OK: return "ok";
+    case W8A16_ERR_M_ZERO: return "m must be >= 1";
+    case W8A16_ERR_K_NOT_MULT_128: return "k must be a positive multiple of 128";
+    case W8A16_ERR_PITCH_TOO_SHORT: return "row pitch shorter than the used extent";
+    case W8A16_ERR_A_STRIDE_ALIGN: return "a_row_stride must be a multiple of 8";
+    case W8A16_ERR_N_ZERO: return "n must be >= 1";
+    case W8A16_ERR_NULL_PTR: return "null pointer argument";
+    case W8A16_ERR_BAD_PLAN: return "plan does not fit the problem";
+    case W8A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+}  // namespace w8a16
+
+extern "C" {
+
+int w8a16_check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
+                     uint32_t c_row_stride)
+{
+    return w8a16::check_args(m, n, k, a_row_stride, c_row_stride);
+}
+
+int w8a16_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    return w8a16::make_plan(m, n, k, cu_count, out);
+}
+
+int w8a16_plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *plan)
+{
+    return w8a16::plan_finalize(m, n, k, plan);
+}
+
+const char *w8a16_status_string(int status) { return w8a16::status_string(status); }
+
+const char *w8a16_last_error(void) { return w8a16::last_error(); }
+
+}  // extern "C"

@@ -1,0 +1,367 @@
+// Weight-streaming W8A16 GEMM kernel for small m (gfx950).
+//
+// Computes C = A * dequant(W)^T with one FP32 scale per 128x128 weight block
+// applied once per 128-wide K step (page "w8a16_gemm_pipelined_m32.rs",
+// doc comments of `w8a16_gemm_pipelined_m32_strided` and
+// `W8A16_M32_K_BLOCK`; module doc, "Numerics").
+//
+// For m <= 64 the operation is bound by reading the FP8 weight from HBM, so
+// the kernel is organised around streaming W once with 16-byte coalesced
+// loads:
+//
+//   * A workgroup (4 waves) owns NBW 16-column blocks of C (16 weight rows
+//     each) and MB 16-row blocks of C, over a range of 128-wide K steps.
+//     Its 4 waves take interleaved K steps (wave w: steps s0+w, s0+w+4, ...),
+//     so at any time the 4 waves read 4 adjacent 128-byte pieces of each
+//     weight row.
+//   * Per K step a wave loads its weight rows (8 lanes per 128-byte row
+//     segment) and the A rows (16 lanes per 256-byte row segment) into
+//     registers, writes them to its private LDS area in an XOR-swizzled
+//     layout, and reads them back in the 16x16x32 BF16 MFMA operand layout.
+//     The next step's loads are issued before the current step's math.
+//   * The weight is the MFMA's first operand (its 16 rows are 16 columns of
+//     C), A is the second; lane l then holds C[m = l%16][n = 4(l/16)..+3],
+//     four adjacent outputs of one row.
+//   * Inside a K step the MFMA's K index is a free relabelling of the 128
+//     physical k: lane group g (= l/16) of MFMA q (0..3) covers physical k
+//     32g+8q..32g+8q+7 in both operands.  That lets each lane read 32
+//     contiguous weight bytes and 64 contiguous A bytes.
+//   * FP8 -> BF16 with v_cvt_scalef32_pk_bf16_fp8 (scale 1.0): every E4M3
+//     value, subnormals included, is a BF16 value, so the dequant is exact.
+//   * Each step's 16x16 MFMA partial starts from zero and is folded into
+//     the FP32 accumulator as acc = fma(scale, partial, acc).
+//   * The 4 waves' accumulators are added in LDS in wave order.  With K
+//     split across workgroups (splits > 1), each split writes its FP32 tile
+//     to a workspace, and the last workgroup to arrive at the tile's counter
+//     adds the splits in split order, so every run gives the same bits.
+//   * Columns and rows past n and m are computed from clamped (valid)
+//     addresses and never stored; A pitch padding is never read.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace w8a16 {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kW = 2048;   // LDS bytes of one 16-row weight block per K step
+constexpr uint32_t kA = 4096;   // LDS bytes of one 16-row A block per K step
+
+// Swizzle of the 16-byte chunk index inside a 128-byte weight row: rows
+// r and r^8 differ in the low bit, so the 16 lanes of one ds_read_b128
+// phase (rows 0..15, same logical chunk) hit distinct banks whether the LDS
+// serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ uint32_t wswz(uint32_t r) { return (r & 7u) ^ (r >> 3); }
+
+// Bytes 0,1 (HI = false) or 2,3 (HI = true) of `raw` -> two BF16 in one dword,
+// the lower byte in the lower half.
+template <bool HI>
+__device__ __forceinline__ uint32_t bf16_pair_from_fp8(uint32_t raw)
+{
+    auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16 FP8 bytes -> two MFMA operands of 8 BF16 (bytes 0..7, bytes 8..15).
+__device__ __forceinline__ void dequant16(u32x4_t raw, bf16x8_t &lo, bf16x8_t &hi)
+{
+    u32x4_t l, h;
+    l.x = bf16_pair_from_fp8<false>(raw.x);
+    l.y = bf16_pair_from_fp8<true>(raw.x);
+    l.z = bf16_pair_from_fp8<false>(raw.y);
+    l.w = bf16_pair_from_fp8<true>(raw.y);
+    h.x = bf16_pair_from_fp8<false>(raw.z);
+    h.y = bf16_pair_from_fp8<true>(raw.z);
+    h.z = bf16_pair_from_fp8<false>(raw.w);
+    h.w = bf16_pair_from_fp8<true>(raw.w);
+    lo = __builtin_bit_cast(bf16x8_t, l);
+    hi = __builtin_bit_cast(bf16x8_t, h);
+}
+
+// Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    __bf16 b = static_cast<__bf16>(f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+// Map the hardware workgroup id to a logical id so that logical ids that
+// are close (the K splits of one tile, then neighbouring tiles) run on the
+// same XCD: workgroups are dispatched round-robin over the 8 XCDs.
+__device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
+{
+    const uint32_t X = 8;
+    const uint32_t q = grid / X, r = grid % X;
+    const uint32_t xcd = bid % X, slot = bid / X;
+    return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Store four adjacent outputs C[row][col..col+3] (FP32 -> BF16).
+__device__ __forceinline__ void store_c4(const GemmArgs &g, f32x4_t v, uint32_t row,
+                                         uint32_t col)
+{
+    if (row >= g.m || col >= g.n)
+        return;
+    uint16_t *dst = reinterpret_cast<uint16_t *>(g.c) + (size_t)row * g.c_stride + col;
+    uint32_t b0 = f32_to_bf16_bits(v.x), b1 = f32_to_bf16_bits(v.y);
+    uint32_t b2 = f32_to_bf16_bits(v.z), b3 = f32_to_bf16_bits(v.w);
+    if (col + 3 < g.n && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+        u32x2_t packed;
+        packed.x = b0 | (b1 << 16);
+        packed.y = b2 | (b3 << 16);
+        *reinterpret_cast<u32x2_t *>(dst) = packed;
+    } else {
+        dst[0] = (uint16_t)b0;
+        if (col + 1 < g.n) dst[1] = (uint16_t)b1;
+        if (col + 2 < g.n) dst[2] = (uint16_t)b2;
+        if (col + 3 < g.n) dst[3] = (uint16_t)b3;
+    }
+}
+
+template <int MB, int NBW>
+__global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
+    const uint32_t split = lid % g.splits;
+    const uint32_t tile = lid / g.splits;
+    const uint32_t m_tile = tile % g.m_tiles;
+    const uint32_t n_tile = tile / g.m_tiles;
+    const uint32_t n0 = n_tile * (NBW * 16);
+    const uint32_t m0 = m_tile * (MB * 16);
+    const uint32_t ksteps = g.k / 128u;
+    const uint32_t s0 = split * g.steps_per_split;
+    const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
+
+    uint8_t *wl = lds + wave * (NBW * kW + MB * kA);
+    uint8_t *al = wl + NBW * kW;
+
+    // ---- loop-invariant addressing -------------------------------------
+    // Global loads: weight row 16j+8h+lane/8 of the tile, 16-byte chunk
+    // lane%8 of the step's 128 bytes; A row 16b+4q+lane/16, chunk lane%16 of
+    // the step's 256 bytes.  Rows past n / m read the last valid row.
+    const uint8_t *wsrc[NBW][2];
+    uint32_t wdst[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t r = 8u * h + (lane >> 3);
+        wdst[h] = r * 128u + (((lane & 7u) ^ wswz(r)) * 16u);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const uint32_t row = min(n0 + 16u * j + r, g.n - 1u);
+            wsrc[j][h] = g.w + (size_t)row * g.k + (lane & 7u) * 16u;
+        }
+    }
+    const uint8_t *asrc[MB][4];
+    uint32_t adst[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t r = 4u * q + (lane >> 4);
+        adst[q] = r * 256u + (((lane & 15u) ^ r) * 16u);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            const uint32_t row = min(m0 + 16u * b + r, g.m - 1u);
+            asrc[b][q] = g.a + (size_t)row * g.a_stride * 2u + (lane & 15u) * 16u;
+        }
+    }
+    // LDS reads in MFMA layout: row r = lane%16, lane group gq = lane/16.
+    const uint32_t rr = lane & 15u, gq = lane >> 4;
+    const uint32_t wrd0 = rr * 128u + (((2u * gq) ^ wswz(rr)) * 16u);
+    const uint32_t wrd1 = rr * 128u + (((2u * gq + 1u) ^ wswz(rr)) * 16u);
+    uint32_t ard[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        ard[q] = rr * 256u + (((4u * gq + q) ^ rr) * 16u);
+    // Scale row of each weight block (a 16-row block never straddles two
+    // 128-row scale blocks).
+    const float *srow[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+        srow[j] = g.scale + (size_t)(min(n0 + 16u * j, g.n - 1u) / 128u) * ksteps;
+
+    f32x4_t acc[NBW][MB];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+            acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wv[NBW][2];
+    u32x4_t av[MB][4];
+    uint32_t t = s0 + wave;
+    if (t < s1) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wv[j][h] = *reinterpret_cast<const u32x4_t *>(wsrc[j][h] + t * 128u);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                av[b][q] = *reinterpret_cast<const u32x4_t *>(asrc[b][q] + t * 256u);
+    }
+
+    for (; t < s1; t += kWavesPerGroup) {
+        // Stage this step through the wave's private LDS area.
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<u32x4_t *>(wl + j * kW + wdst[h]) = wv[j][h];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x4_t *>(al + b * kA + adst[q]) = av[b][q];
+
+        // Issue the next step's loads before the math of this one.
+        const uint32_t tn = t + kWavesPerGroup;
+        if (tn < s1) {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wv[j][h] = *reinterpret_cast<const u32x4_t *>(wsrc[j][h] + tn * 128u);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    av[b][q] = *reinterpret_cast<const u32x4_t *>(asrc[b][q] + tn * 256u);
+        }
+
+        bf16x8_t af[MB][4];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                af[b][q] = *reinterpret_cast<const bf16x8_t *>(al + b * kA + ard[q]);
+
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd0);
+            const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd1);
+            bf16x8_t wb[4];
+            dequant16(r0, wb[0], wb[1]);
+            dequant16(r1, wb[2], wb[3]);
+            const float s = srow[j][t];
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[q], af[b][q], p, 0, 0, 0);
+                acc[j][b].x = __builtin_fmaf(s, p.x, acc[j][b].x);
+                acc[j][b].y = __builtin_fmaf(s, p.y, acc[j][b].y);
+                acc[j][b].z = __builtin_fmaf(s, p.z, acc[j][b].z);
+                acc[j][b].w = __builtin_fmaf(s, p.w, acc[j][b].w);
+            }
+        }
+    }
+
+    // ---- add the 4 waves' partial sums in wave order ---------------------
+    constexpr int P = NBW * MB;
+    __syncthreads();
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+            red[(wave * P + j * MB + b) * 64 + lane] = acc[j][b];
+    __syncthreads();
+
+    // Output position of a lane for pair (j, b).
+    const uint32_t out_row_off = lane & 15u;
+    const uint32_t out_col_off = 4u * (lane >> 4);
+
+    if (g.splits == 1) {
+        for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
+            f32x4_t s = red[pi * 64 + lane];
+#pragma unroll
+            for (uint32_t w = 1; w < kWavesPerGroup; ++w)
+                s += red[(w * P + pi) * 64 + lane];
+            const uint32_t j = pi / MB, b = pi % MB;
+            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+        }
+        return;
+    }
+
+    // ---- split-K: publish this split's tile, the last arrival adds all ----
+    f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
+    for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
+        f32x4_t s = red[pi * 64 + lane];
+#pragma unroll
+        for (uint32_t w = 1; w < kWavesPerGroup; ++w)
+            s += red[(w * P + pi) * 64 + lane];
+        ws_tile[((size_t)split * P + pi) * 64 + lane] = s;
+    }
+    __threadfence();
+    __syncthreads();
+    __shared__ uint32_t last;
+    if (threadIdx.x == 0) {
+        const uint32_t prev = atomicAdd(g.counters + tile, 1u);
+        last = (prev == g.splits - 1u) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!last)
+        return;
+    __threadfence();
+    for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
+        f32x4_t s = ws_tile[pi * 64 + lane];
+        for (uint32_t sp = 1; sp < g.splits; ++sp)
+            s += ws_tile[((size_t)sp * P + pi) * 64 + lane];
+        const uint32_t j = pi / MB, b = pi % MB;
+        store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+    }
+    if (threadIdx.x == 0)
+        atomicExch(g.counters + tile, 0u);   // ready for the next call on this stream
+}
+
+template <int MB, int NBW>
+hipError_t launch_stream_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    auto kern = w8a16_stream_kernel<MB, NBW>;
+    static bool attr_set = false;
+    if (p.lds_bytes > 65536 && !attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)p.lds_bytes);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    switch (p.m_blocks * 100 + p.n_blocks) {
+    case 101: return launch_stream_t<1, 1>(g, p, stream);
+    case 102: return launch_stream_t<1, 2>(g, p, stream);
+    case 104: return launch_stream_t<1, 4>(g, p, stream);
+    case 108: return launch_stream_t<1, 8>(g, p, stream);
+    case 201: return launch_stream_t<2, 1>(g, p, stream);
+    case 202: return launch_stream_t<2, 2>(g, p, stream);
+    case 204: return launch_stream_t<2, 4>(g, p, stream);
+    case 208: return launch_stream_t<2, 8>(g, p, stream);
+    case 401: return launch_stream_t<4, 1>(g, p, stream);
+    case 402: return launch_stream_t<4, 2>(g, p, stream);
+    case 404: return launch_stream_t<4, 4>(g, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w8a16

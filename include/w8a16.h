@@ -1,0 +1,139 @@
+/*
+ * w8a16.h -- C ABI of the block-scaled FP8 W8A16 small-M GEMM for MI355X
+ * (gfx950).
+ *
+ * The operation (page "w8a16_gemm_pipelined_m32.rs", doc comment of
+ * `w8a16_gemm_pipelined_m32_strided`; one FP8 scale block per 128-wide K
+ * step, doc comment of `W8A16_M32_K_BLOCK`):
+ *
+ *   C[i][j] = bf16( sum_{b < K/128} S[j/128][b] * sum_{t < 128} A[i][128b+t] * W[j][128b+t] )
+ *
+ *   A  BF16 (bits, 2 bytes)   [m, a_row_stride]   first k elements of each row are read
+ *   W  FP8 E4M3 (OCP E4M3FN)  [n, k]              row-major, contiguous, 1 byte per weight
+ *   S  FP32                   [ceil(n/128), k/128] row-major: scale of W block (j/128, k/128)
+ *   C  BF16                   [m, c_row_stride]   first n elements of each row are written
+ *
+ * Strides are in elements.  Products are taken in BF16 x BF16 with FP32
+ * accumulation; each 128-wide K step's partial sum is multiplied by its
+ * block scale once and added in FP32; the result is rounded to BF16 with
+ * round-to-nearest-even.  The association of the K reduction inside a step,
+ * across the waves of a workgroup and across K splits is fixed by the plan,
+ * so a given plan gives the same bits on every run.
+ *
+ * Ownership: every pointer passed to w8a16_gemm* is a DEVICE pointer owned
+ * by the caller, who keeps the buffers alive until the stream has passed
+ * the call.  The library keeps no pointer to them.  It owns one split-K
+ * workspace and counter array per (device, stream), allocated with
+ * hipMalloc on first use and grown when a larger plan needs it; make one
+ * call on a stream before capturing that stream into a HIP graph.
+ *
+ * Alignment and aliasing: A, W, S and C must be 16-byte aligned (torch
+ * allocations are).  C must not overlap A, W or S.  c_row_stride may be any
+ * value >= n.
+ *
+ * Errors: every entry point returns a w8a16_status.  Argument errors are
+ * detected before anything is enqueued, in the order of the enum below
+ * (codes 1..4 in the order the page checks them; 5..7 are checks the page
+ * does not make).  w8a16_last_error() then holds a message for the calling
+ * thread.  Launches are asynchronous: the call returns once the kernel is
+ * enqueued on `stream`; a failed enqueue returns W8A16_ERR_HIP.
+ */
+#ifndef W8A16_H
+#define W8A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a16_status {
+    W8A16_OK = 0,
+    W8A16_ERR_M_ZERO = 1,            /* m == 0: no rows to compute */
+    W8A16_ERR_K_NOT_MULT_128 = 2,    /* k == 0 or k % 128 != 0 */
+    W8A16_ERR_PITCH_TOO_SHORT = 3,   /* a_row_stride < k or c_row_stride < n */
+    W8A16_ERR_A_STRIDE_ALIGN = 4,    /* a_row_stride % 8 != 0 (16-byte rows) */
+    W8A16_ERR_N_ZERO = 5,            /* n == 0: empty launch */
+    W8A16_ERR_NULL_PTR = 6,          /* a, w_fp8, block_scale or c is null */
+    W8A16_ERR_BAD_PLAN = 7,          /* a plan that does not fit the problem */
+    W8A16_ERR_HIP = 8                /* allocation or launch failed in HIP */
+} w8a16_status;
+
+/* Kernel families a plan can name. */
+typedef enum w8a16_kernel {
+    /* Weight-streaming kernel: a workgroup owns n_blocks 16-column blocks
+     * of C and m_blocks 16-row blocks, its 4 waves take interleaved 128-wide
+     * K steps, and K may be split across workgroups with a fixed-order
+     * FP32 fix-up. */
+    W8A16_KERNEL_STREAM = 1,
+    /* Tiled kernel for large m: a workgroup owns a 128-row x n_blocks*16
+     * column tile of C, shares the A and dequantized W tiles of each K step
+     * through LDS, and its waves split the tile, not K. */
+    W8A16_KERNEL_TILE = 2
+} w8a16_kernel;
+
+/* Launch plan.  w8a16_plan() fills every field; callers may change
+ * kernel, m_blocks, n_blocks and splits and pass the result to
+ * w8a16_gemm_planned(), which recomputes the derived fields and rejects a
+ * plan the kernels do not support (W8A16_ERR_BAD_PLAN). */
+typedef struct w8a16_plan {
+    uint32_t kernel;          /* w8a16_kernel */
+    uint32_t m_blocks;        /* 16-row blocks of C per workgroup tile */
+    uint32_t n_blocks;        /* 16-column blocks of C per workgroup tile */
+    uint32_t splits;          /* K splits across workgroups (>= 1) */
+    uint32_t steps_per_split; /* 128-wide K steps per split (derived) */
+    uint32_t m_tiles;         /* ceil(m / (16 * m_blocks)) (derived) */
+    uint32_t n_tiles;         /* ceil(n / (16 * n_blocks)) (derived) */
+    uint32_t grid;            /* workgroups launched (derived) */
+    uint32_t block;           /* threads per workgroup (derived) */
+    uint32_t lds_bytes;       /* LDS per workgroup (derived) */
+    uint64_t workspace_bytes; /* split-K FP32 partials (derived; 0 if splits == 1) */
+    uint32_t counter_count;   /* split-K arrival counters (derived) */
+    uint32_t cu_count;        /* compute units the plan was sized for */
+} w8a16_plan_t;
+
+/* Validate the scalar arguments alone, in the documented order.  Pure: no
+ * GPU call.  Returns W8A16_OK or the first failing check's code. */
+int w8a16_check_args(uint32_t m, uint32_t n, uint32_t k,
+                     uint32_t a_row_stride, uint32_t c_row_stride);
+
+/* Default plan for (m, n, k) on a device with `cu_count` compute units
+ * (0 means 256, MI355X).  Pure: no GPU call.  Checks m, n and k as
+ * w8a16_check_args does (pitches are not part of a plan). */
+int w8a16_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count,
+               w8a16_plan_t *out);
+
+/* Recompute the derived fields of a caller-edited plan and check it.
+ * Pure: no GPU call. */
+int w8a16_plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *plan);
+
+/* The GEMM.  a: BF16 [m, a_row_stride]; w_fp8: E4M3 [n, k]; block_scale:
+ * FP32 [ceil(n/128), k/128]; c: BF16 [m, c_row_stride].  All device
+ * pointers.  stream: a hipStream_t (NULL for the null stream).  Picks the
+ * plan with w8a16_plan() for the current device's CU count. */
+int w8a16_gemm(const void *a, uint32_t a_row_stride,
+               const void *w_fp8, const float *block_scale,
+               void *c, uint32_t c_row_stride,
+               uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* The GEMM with an explicit plan (kernel, m_blocks, n_blocks, splits taken
+ * from *plan; derived fields recomputed).  For tests and tuning: every
+ * valid plan computes the same operation; plans differ only in the order of
+ * the FP32 additions. */
+int w8a16_gemm_planned(const void *a, uint32_t a_row_stride,
+                       const void *w_fp8, const float *block_scale,
+                       void *c, uint32_t c_row_stride,
+                       uint32_t m, uint32_t n, uint32_t k,
+                       const w8a16_plan_t *plan, void *stream);
+
+/* Static text for a status code (never null). */
+const char *w8a16_status_string(int status);
+
+/* Message of the calling thread's last failing call ("" if none). */
+const char *w8a16_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A16_H */

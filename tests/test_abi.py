@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+include/w8a16.h declares, rejects bad arguments in the documented order
+before touching the GPU, and plans that cover the problem exactly."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_scaled_fp8_w8a16_amd as w8
+from block_scaled_fp8_w8a16_amd import Plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a16.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a16_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = w8.library()
+    declared = _declared_functions()
+    assert set(declared) == set(w8.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", w8.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(w8a16_\w+)", out))
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    for code in range(0, 9):
+        assert w8.status_string(code)
+    assert w8.status_string(1234) == "unknown status"
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 16, 128, 128, 16), w8.ERR_M_ZERO),
+    ((0, 0, 100, 0, 0), w8.ERR_M_ZERO),            # m first
+    ((1, 16, 0, 128, 16), w8.ERR_K_NOT_MULT_128),
+    ((1, 16, 100, 128, 16), w8.ERR_K_NOT_MULT_128),
+    ((1, 16, 100, 4, 0), w8.ERR_K_NOT_MULT_128),   # k before pitches
+    ((1, 16, 256, 128, 16), w8.ERR_PITCH_TOO_SHORT),
+    ((1, 16, 256, 256, 15), w8.ERR_PITCH_TOO_SHORT),
+    ((1, 16, 256, 260, 15), w8.ERR_PITCH_TOO_SHORT),  # pitches before alignment
+    ((1, 16, 256, 260, 16), w8.ERR_A_STRIDE_ALIGN),
+    ((1, 0, 256, 260, 0), w8.ERR_A_STRIDE_ALIGN),  # alignment before n == 0
+    ((1, 0, 256, 256, 0), w8.ERR_N_ZERO),
+    ((1, 16, 256, 264, 17), w8.OK),
+    ((32, 6144, 2048, 2560, 8192), w8.OK),
+])
+def test_check_args_order(args, want):
+    assert w8.check_args(*args) == want
+
+
+def test_gemm_rejects_before_any_gpu_call():
+    # Argument errors return before HIP is touched, so they work on a host
+    # without a GPU; the message follows the page's wording.
+    st = w8.gemm_raw(0, 128, 0, 0, 0, 16, 0, 16, 128)
+    assert st == w8.ERR_M_ZERO
+    assert "m=0 has no rows" in w8.last_error()
+    st = w8.gemm_raw(0, 128, 0, 0, 0, 16, 1, 16, 130)
+    assert st == w8.ERR_K_NOT_MULT_128
+    assert "K=130 must be a positive multiple of 128" in w8.last_error()
+    st = w8.gemm_raw(0, 100, 0, 0, 0, 16, 1, 16, 128)
+    assert st == w8.ERR_PITCH_TOO_SHORT
+    st = w8.gemm_raw(0, 132, 0, 0, 0, 16, 1, 16, 128)
+    assert st == w8.ERR_A_STRIDE_ALIGN
+    st = w8.gemm_raw(0, 128, 0, 0, 0, 16, 1, 16, 128)
+    assert st == w8.ERR_NULL_PTR
+    p = w8.plan(1, 16, 128)
+    st = w8.gemm_raw(0, 128, 0, 0, 0, 16, 1, 16, 128, plan_=p)
+    assert st == w8.ERR_NULL_PTR
+
+
+def _covers(p: Plan, m, n, k):
+    """Every (m block, n block, K step) is owned by exactly one workgroup."""
+    ksteps = k // 128
+    assert p.splits * p.steps_per_split >= ksteps
+    assert (p.splits - 1) * p.steps_per_split < ksteps
+    assert p.m_tiles * 16 * p.m_blocks >= m > (p.m_tiles - 1) * 16 * p.m_blocks
+    assert p.n_tiles * 16 * p.n_blocks >= n > (p.n_tiles - 1) * 16 * p.n_blocks
+    assert p.grid == p.m_tiles * p.n_tiles * p.splits
+    owned = {}
+    for s in range(p.splits):
+        for t in range(s * p.steps_per_split, min(ksteps, (s + 1) * p.steps_per_split)):
+            owned[t] = owned.get(t, 0) + 1
+    assert sorted(owned) == list(range(ksteps))
+    assert set(owned.values()) == {1}
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 256), (8, 4096, 4096), (16, 12288, 5120),
+                                   (32, 6144, 2048), (128, 8192, 8192), (1, 1, 128),
+                                   (40, 1000, 384), (64, 17, 128 * 37),
+                                   (65, 300, 1024), (3, 70000, 128)])
+def test_default_plans_cover_the_problem(m, n, k):
+    p = w8.plan(m, n, k)
+    _covers(p, m, n, k)
+    assert p.block in (256,)
+    assert p.lds_bytes <= 160 * 1024
+    if p.splits > 1:
+        assert p.workspace_bytes == p.grid * p.m_blocks * p.n_blocks * 1024
+        assert p.counter_count == p.m_tiles * p.n_tiles
+    else:
+        assert p.workspace_bytes == 0
+
+
+def test_small_m_plans_stream_kernel_and_fill_the_chip():
+    for m, n, k in [(8, 4096, 4096), (16, 12288, 5120), (32, 6144, 2048)]:
+        p = w8.plan(m, n, k)
+        assert p.kernel == w8.KERNEL_STREAM
+        assert p.m_blocks == (1 if m <= 16 else 2)
+        assert p.grid >= 256
+
+
+def test_explicit_plans():
+    p = w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 8)
+    _covers(p, 16, 4096, 4096)
+    assert p.splits == 8 and p.steps_per_split == 4
+    p = w8.make_plan(16, 4096, 128 * 33, w8.KERNEL_STREAM, 1, 2, 5)
+    _covers(p, 16, 4096, 128 * 33)
+    assert (p.splits, p.steps_per_split) == (5, 7)
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 3, 4, 1)
+    assert e.value.status == w8.ERR_BAD_PLAN
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 33)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(16, 4096, 4096, 99, 1, 4, 1)
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.make_plan(0, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 1)
+    assert e.value.status == w8.ERR_M_ZERO
