@@ -70,9 +70,14 @@ static uint32_t div_up(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
 static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 {
-    bool mb_ok = mb == 1 || mb == 2 || mb == 4;
-    bool nb_ok = nb == 1 || nb == 2 || nb == 4 || nb == 8;
-    return mb_ok && nb_ok && mb * nb <= 16;
+    switch (mb * 100 + nb) {
+    case 101: case 102: case 104: case 108:
+    case 201: case 202: case 204:
+    case 401: case 402:
+        return true;
+    default:
+        return false;
+    }
 }
 
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
@@ -98,11 +103,30 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        p->block = kWaves * 64;
-        uint32_t per_wave = p->n_blocks * kWBlockBytes + p->m_blocks * kABlockBytes;
-        uint32_t staging = kWaves * per_wave;
-        uint32_t reduce = kWaves * p->n_blocks * p->m_blocks * kAccBytes;
+        if (p->depth != 1 && p->depth != 2 && p->depth != 4) {
+            snprintf(buf, sizeof buf, "w8a16_plan: depth=%u must be 1, 2 or 4", p->depth);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        if (p->flags & ~(uint32_t)W8A16_FLAG_DIRECT) {
+            snprintf(buf, sizeof buf, "w8a16_plan: unknown flags 0x%x", p->flags);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        if (p->waves != 4 && p->waves != 8 && p->waves != 16) {
+            snprintf(buf, sizeof buf, "w8a16_plan: waves=%u must be 4, 8 or 16", p->waves);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->block = p->waves * 64;
+        const bool direct = (p->flags & W8A16_FLAG_DIRECT) != 0;
+        uint32_t per_wave = p->n_blocks * kWBlockBytes + (direct ? 0u : p->m_blocks * kABlockBytes);
+        uint32_t staging = p->waves * per_wave;
+        uint32_t reduce = p->waves * p->n_blocks * p->m_blocks * kAccBytes;
         p->lds_bytes = staging > reduce ? staging : reduce;
+        if (p->lds_bytes > kMaxLdsBytes) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
+                     p->lds_bytes, kMaxLdsBytes);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
     } else if (p->kernel == W8A16_KERNEL_TILE && kTileKernelBuilt) {
         if (!tile_shape_supported(p->m_blocks, p->n_blocks)) {
             snprintf(buf, sizeof buf,
@@ -157,7 +181,6 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     p.cu_count = cu_count ? cu_count : kDefaultCUs;
     const uint32_t ksteps = k / kKStep;
     const uint32_t nb16 = div_up(n, 16);
-    const uint32_t target = 2 * p.cu_count;   // workgroups wanted in flight
 
     if (m > 64 && kTileKernelBuilt) {
         // Large m: 128-row tiles with the dequantized weight tile shared by
@@ -170,28 +193,39 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         while (tiles * p.splits < p.cu_count && ksteps / (p.splits * 2) >= 8)
             p.splits *= 2;
     } else {
+        // Small m: the weight-streaming kernel.  Measured on MI355X, the
+        // best plans give each CU about one workgroup tile, enough waves
+        // that every wave has only a few K steps (so a CU's whole share of
+        // the weight is requested in about one memory round trip), and no K
+        // split across workgroups: the agent-scope release that publishing a
+        // split partial needs writes back the L2 and costs far more than it
+        // saves.
         p.kernel = W8A16_KERNEL_STREAM;
+        p.depth = 1;
+        p.flags = 0;
         p.m_blocks = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
         const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
-        // Widest column tile that still gives every CU a workgroup; the
-        // weight is read once whatever the tile, wider tiles only cut the
-        // re-reads of A.
+        const uint32_t fill = (3 * p.cu_count) / 4;
         uint32_t nbw = 1;
         const uint32_t cands[3] = {4, 2, 1};
         for (uint32_t c : cands) {
-            if (p.m_blocks * c > 16)
+            if (!stream_shape_supported(p.m_blocks, c))
                 continue;
-            if (div_up(nb16, c) * m_tiles >= p.cu_count) {
+            if (div_up(nb16, c) * m_tiles >= fill) {
                 nbw = c;
                 break;
             }
         }
         p.n_blocks = nbw;
-        uint32_t tiles = div_up(nb16, nbw) * m_tiles;
-        // Split K until there are `target` workgroups, keeping at least one
-        // K step per wave in every split.
+        const uint32_t pairs = p.m_blocks * p.n_blocks;
+        p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
+        while (p.waves > 4 && ksteps < 2 * p.waves)
+            p.waves /= 2;
+        const uint32_t tiles = div_up(nb16, nbw) * m_tiles;
+        // Split K only when the tiles would leave most CUs idle and every
+        // split still gives each wave two or more K steps.
         p.splits = 1;
-        while (tiles * p.splits < target && ksteps / (p.splits * 2) >= kWaves)
+        while (tiles * p.splits * 2 <= p.cu_count && ksteps >= 4 * p.waves * p.splits)
             p.splits *= 2;
     }
     st = plan_finalize(m, n, k, &p);

@@ -13,6 +13,9 @@ constexpr uint32_t kWBlockBytes = 16 * 128;      // 16 weight rows x one K step 
 constexpr uint32_t kABlockBytes = 16 * 128 * 2;  // 16 A rows x one K step (BF16)
 constexpr uint32_t kAccBytes = 64 * 4 * 4;       // one 16x16 FP32 MFMA tile
 constexpr uint32_t kDefaultCUs = 256;            // MI355X
+// Dynamic LDS a plan may use: the 160 KiB of a gfx950 CU less room for the
+// kernels' small static __shared__ variables.
+constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 256;
 constexpr uint32_t kTileThreads = 256;           // tile kernel: 4 waves
 constexpr bool kTileKernelBuilt = false;
 

@@ -125,13 +125,31 @@ __device__ __forceinline__ void store_c4(const GemmArgs &g, f32x4_t v, uint32_t 
     }
 }
 
-template <int MB, int NBW>
-__global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
+// Sum of the WAVES partial tiles of pair `pi` for one lane, in wave order.
+// All LDS reads are issued before the additions.
+template <int WAVES, int P>
+__device__ __forceinline__ f32x4_t sum_waves(const f32x4_t *red, uint32_t pi, uint32_t lane)
+{
+    f32x4_t v[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+        v[w] = red[(w * P + pi) * 64 + lane];
+    f32x4_t s = v[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w)
+        s += v[w];
+    return s;
+}
+
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
+    // The wave index is the same for all lanes of a wave; saying so lets the
+    // per-step scale loads be scalar loads.
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
     const uint32_t split = lid % g.splits;
     const uint32_t tile = lid / g.splits;
@@ -142,14 +160,23 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
     const uint32_t ksteps = g.k / 128u;
     const uint32_t s0 = split * g.steps_per_split;
     const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
+    // This wave's K steps: first, first + 4, first + 8, ... (nw of them).
+    const uint32_t first = s0 + wave;
+    const uint32_t nw = first < s1 ? (s1 - first + WAVES - 1) / WAVES : 0u;
 
-    uint8_t *wl = lds + wave * (NBW * kW + MB * kA);
+    uint8_t *wl = lds + wave * (NBW * kW + (DIRECT ? 0u : MB * kA));
     uint8_t *al = wl + NBW * kW;
 
+    // MFMA operand layout: row rr = lane%16 of a 16-row block, lane group
+    // gq = lane/16 covers physical k 32gq..32gq+31 of the step.
+    const uint32_t rr = lane & 15u, gq = lane >> 4;
+
     // ---- loop-invariant addressing -------------------------------------
-    // Global loads: weight row 16j+8h+lane/8 of the tile, 16-byte chunk
-    // lane%8 of the step's 128 bytes; A row 16b+4q+lane/16, chunk lane%16 of
-    // the step's 256 bytes.  Rows past n / m read the last valid row.
+    // DIRECT: each lane loads its own operand bytes (weight: 32 bytes of row
+    // n0+16j+rr; A: 64 bytes of row m0+16b+rr).  Otherwise loads are
+    // coalesced (weight row 16j+8h+lane/8, 16-byte chunk lane%8; A row
+    // 16b+4q+lane/16, chunk lane%16) and go through the wave's LDS area.
+    // Weight rows past n read the last valid row; A rows past m are zero.
     const uint8_t *wsrc[NBW][2];
     uint32_t wdst[2];
 #pragma unroll
@@ -163,19 +190,22 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
         }
     }
     const uint8_t *asrc[MB][4];
-    uint32_t adst[4];
+    bool aok[MB][4];
+    uint32_t adst[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t r = 4u * q + (lane >> 4);
-        adst[q] = r * 256u + (((lane & 15u) ^ r) * 16u);
+        const uint32_t r = DIRECT ? rr : 4u * q + (lane >> 4);
+        if (!DIRECT)
+            adst[q] = r * 256u + (((lane & 15u) ^ r) * 16u);
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
-            const uint32_t row = min(m0 + 16u * b + r, g.m - 1u);
-            asrc[b][q] = g.a + (size_t)row * g.a_stride * 2u + (lane & 15u) * 16u;
+            const uint32_t row = m0 + 16u * b + r;
+            aok[b][q] = row < g.m;
+            asrc[b][q] = g.a + (size_t)min(row, g.m - 1u) * g.a_stride * 2u +
+                         (DIRECT ? (4u * gq + q) * 16u : (lane & 15u) * 16u);
         }
     }
-    // LDS reads in MFMA layout: row r = lane%16, lane group gq = lane/16.
-    const uint32_t rr = lane & 15u, gq = lane >> 4;
+    // LDS reads in MFMA layout (staged mode only).
     const uint32_t wrd0 = rr * 128u + (((2u * gq) ^ wswz(rr)) * 16u);
     const uint32_t wrd1 = rr * 128u + (((2u * gq + 1u) ^ wswz(rr)) * 16u);
     uint32_t ard[4];
@@ -196,75 +226,97 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
         for (int b = 0; b < MB; ++b)
             acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t wv[NBW][2];
-    u32x4_t av[MB][4];
-    uint32_t t = s0 + wave;
-    if (t < s1) {
+    // Ring of DEPTH K steps in flight per wave.
+    u32x4_t wr[DEPTH][NBW][2];
+    u32x4_t ar[DEPTH][MB][4];
+    float sr[DEPTH][NBW];
+
+    auto issue = [&](int d, uint32_t t) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                wv[j][h] = *reinterpret_cast<const u32x4_t *>(wsrc[j][h] + t * 128u);
+                wr[d][j][h] = *reinterpret_cast<const u32x4_t *>(wsrc[j][h] + t * 128u);
 #pragma unroll
         for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                av[b][q] = *reinterpret_cast<const u32x4_t *>(asrc[b][q] + t * 256u);
-    }
-
-    for (; t < s1; t += kWavesPerGroup) {
-        // Stage this step through the wave's private LDS area.
+                ar[d][b][q] = aok[b][q]
+                    ? *reinterpret_cast<const u32x4_t *>(asrc[b][q] + t * 256u)
+                    : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<u32x4_t *>(wl + j * kW + wdst[h]) = wv[j][h];
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x4_t *>(al + b * kA + adst[q]) = av[b][q];
+            sr[d][j] = srow[j][t];
+    };
 
-        // Issue the next step's loads before the math of this one.
-        const uint32_t tn = t + kWavesPerGroup;
-        if (tn < s1) {
 #pragma unroll
-            for (int j = 0; j < NBW; ++j)
+    for (int d = 0; d < DEPTH; ++d)
+        if ((uint32_t)d < nw)
+            issue(d, first + WAVES * d);
+
+    for (uint32_t base = 0; base < nw; base += DEPTH) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    wv[j][h] = *reinterpret_cast<const u32x4_t *>(wsrc[j][h] + tn * 128u);
+        for (int d = 0; d < DEPTH; ++d) {
+            const uint32_t i = base + d;
+            if (i >= nw)
+                break;
+            // Take step i out of the ring and refill the slot with step
+            // i + DEPTH before doing step i's math.
+            u32x4_t cw[NBW][2];
+            u32x4_t ca[MB][4];
+            float cs[NBW];
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                cw[j][0] = wr[d][j][0];
+                cw[j][1] = wr[d][j][1];
+                cs[j] = sr[d][j];
+            }
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    av[b][q] = *reinterpret_cast<const u32x4_t *>(asrc[b][q] + tn * 256u);
-        }
+                    ca[b][q] = ar[d][b][q];
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    *reinterpret_cast<u32x4_t *>(wl + j * kW + wdst[h]) = cw[j][h];
+            if (!DIRECT) {
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<u32x4_t *>(al + b * kA + adst[q]) = ca[b][q];
+            }
+            if (i + DEPTH < nw)
+                issue(d, first + WAVES * (i + DEPTH));
 
-        bf16x8_t af[MB][4];
+            bf16x8_t af[MB][4];
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                af[b][q] = *reinterpret_cast<const bf16x8_t *>(al + b * kA + ard[q]);
-
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd0);
-            const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd1);
-            bf16x8_t wb[4];
-            dequant16(r0, wb[0], wb[1]);
-            dequant16(r1, wb[2], wb[3]);
-            const float s = srow[j][t];
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < MB; ++b)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[q], af[b][q], p, 0, 0, 0);
-                acc[j][b].x = __builtin_fmaf(s, p.x, acc[j][b].x);
-                acc[j][b].y = __builtin_fmaf(s, p.y, acc[j][b].y);
-                acc[j][b].z = __builtin_fmaf(s, p.z, acc[j][b].z);
-                acc[j][b].w = __builtin_fmaf(s, p.w, acc[j][b].w);
+                    af[b][q] = DIRECT
+                        ? __builtin_bit_cast(bf16x8_t, ca[b][q])
+                        : *reinterpret_cast<const bf16x8_t *>(al + b * kA + ard[q]);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd0);
+                const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(wl + j * kW + wrd1);
+                bf16x8_t wb[4];
+                dequant16(r0, wb[0], wb[1]);
+                dequant16(r1, wb[2], wb[3]);
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[q], af[b][q], p, 0, 0, 0);
+                    acc[j][b].x = __builtin_fmaf(cs[j], p.x, acc[j][b].x);
+                    acc[j][b].y = __builtin_fmaf(cs[j], p.y, acc[j][b].y);
+                    acc[j][b].z = __builtin_fmaf(cs[j], p.z, acc[j][b].z);
+                    acc[j][b].w = __builtin_fmaf(cs[j], p.w, acc[j][b].w);
+                }
             }
         }
     }
@@ -285,11 +337,8 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
     const uint32_t out_col_off = 4u * (lane >> 4);
 
     if (g.splits == 1) {
-        for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
-            f32x4_t s = red[pi * 64 + lane];
-#pragma unroll
-            for (uint32_t w = 1; w < kWavesPerGroup; ++w)
-                s += red[(w * P + pi) * 64 + lane];
+        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+            const f32x4_t s = sum_waves<WAVES, P>(red, pi, lane);
             const uint32_t j = pi / MB, b = pi % MB;
             store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
         }
@@ -298,13 +347,8 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
 
     // ---- split-K: publish this split's tile, the last arrival adds all ----
     f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
-    for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
-        f32x4_t s = red[pi * 64 + lane];
-#pragma unroll
-        for (uint32_t w = 1; w < kWavesPerGroup; ++w)
-            s += red[(w * P + pi) * 64 + lane];
-        ws_tile[((size_t)split * P + pi) * 64 + lane] = s;
-    }
+    for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES)
+        ws_tile[((size_t)split * P + pi) * 64 + lane] = sum_waves<WAVES, P>(red, pi, lane);
     __threadfence();
     __syncthreads();
     __shared__ uint32_t last;
@@ -316,7 +360,7 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
     if (!last)
         return;
     __threadfence();
-    for (uint32_t pi = wave; pi < (uint32_t)P; pi += kWavesPerGroup) {
+    for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
         f32x4_t s = ws_tile[pi * 64 + lane];
         for (uint32_t sp = 1; sp < g.splits; ++sp)
             s += ws_tile[((size_t)sp * P + pi) * 64 + lane];
@@ -327,10 +371,10 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(GemmArgs g)
         atomicExch(g.counters + tile, 0u);   // ready for the next call on this stream
 }
 
-template <int MB, int NBW>
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
 hipError_t launch_stream_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    auto kern = w8a16_stream_kernel<MB, NBW>;
+    auto kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -344,22 +388,46 @@ hipError_t launch_stream_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t
     return hipGetLastError();
 }
 
+template <int MB, int NBW, int DEPTH, bool DIRECT>
+hipError_t launch_stream_w(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    switch (p.block / 64) {
+    case 4: return launch_stream_t<MB, NBW, DEPTH, DIRECT, 4>(g, p, stream);
+    case 8: return launch_stream_t<MB, NBW, DEPTH, DIRECT, 8>(g, p, stream);
+    case 16: return launch_stream_t<MB, NBW, DEPTH, DIRECT, 16>(g, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int MB, int NBW>
+hipError_t launch_stream_mn(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    const bool direct = (p.flags & W8A16_FLAG_DIRECT) != 0;
+    switch (p.depth * 2 + (direct ? 1 : 0)) {
+    case 2: return launch_stream_w<MB, NBW, 1, false>(g, p, stream);
+    case 3: return launch_stream_w<MB, NBW, 1, true>(g, p, stream);
+    case 4: return launch_stream_w<MB, NBW, 2, false>(g, p, stream);
+    case 5: return launch_stream_w<MB, NBW, 2, true>(g, p, stream);
+    case 8: return launch_stream_w<MB, NBW, 4, false>(g, p, stream);
+    case 9: return launch_stream_w<MB, NBW, 4, true>(g, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     switch (p.m_blocks * 100 + p.n_blocks) {
-    case 101: return launch_stream_t<1, 1>(g, p, stream);
-    case 102: return launch_stream_t<1, 2>(g, p, stream);
-    case 104: return launch_stream_t<1, 4>(g, p, stream);
-    case 108: return launch_stream_t<1, 8>(g, p, stream);
-    case 201: return launch_stream_t<2, 1>(g, p, stream);
-    case 202: return launch_stream_t<2, 2>(g, p, stream);
-    case 204: return launch_stream_t<2, 4>(g, p, stream);
-    case 208: return launch_stream_t<2, 8>(g, p, stream);
-    case 401: return launch_stream_t<4, 1>(g, p, stream);
-    case 402: return launch_stream_t<4, 2>(g, p, stream);
-    case 404: return launch_stream_t<4, 4>(g, p, stream);
+    case 101: return launch_stream_mn<1, 1>(g, p, stream);
+    case 102: return launch_stream_mn<1, 2>(g, p, stream);
+    case 104: return launch_stream_mn<1, 4>(g, p, stream);
+    case 108: return launch_stream_mn<1, 8>(g, p, stream);
+    case 201: return launch_stream_mn<2, 1>(g, p, stream);
+    case 202: return launch_stream_mn<2, 2>(g, p, stream);
+    case 204: return launch_stream_mn<2, 4>(g, p, stream);
+    case 401: return launch_stream_mn<4, 1>(g, p, stream);
+    case 402: return launch_stream_mn<4, 2>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

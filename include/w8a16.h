@@ -62,7 +62,7 @@ typedef enum w8a16_status {
 /* Kernel families a plan can name. */
 typedef enum w8a16_kernel {
     /* Weight-streaming kernel: a workgroup owns n_blocks 16-column blocks
-     * of C and m_blocks 16-row blocks, its 4 waves take interleaved 128-wide
+     * of C and m_blocks 16-row blocks, its waves take interleaved 128-wide
      * K steps, and K may be split across workgroups with a fixed-order
      * FP32 fix-up. */
     W8A16_KERNEL_STREAM = 1,
@@ -73,7 +73,7 @@ typedef enum w8a16_kernel {
 } w8a16_kernel;
 
 /* Launch plan.  w8a16_plan() fills every field; callers may change
- * kernel, m_blocks, n_blocks and splits and pass the result to
+ * kernel, m_blocks, n_blocks, splits, depth, flags and waves and pass the result to
  * w8a16_gemm_planned(), which recomputes the derived fields and rejects a
  * plan the kernels do not support (W8A16_ERR_BAD_PLAN). */
 typedef struct w8a16_plan {
@@ -90,7 +90,17 @@ typedef struct w8a16_plan {
     uint64_t workspace_bytes; /* split-K FP32 partials (derived; 0 if splits == 1) */
     uint32_t counter_count;   /* split-K arrival counters (derived) */
     uint32_t cu_count;        /* compute units the plan was sized for */
+    uint32_t depth;           /* K steps each wave keeps in flight (1, 2 or 4) */
+    uint32_t flags;           /* W8A16_FLAG_* bits */
+    uint32_t waves;           /* waves per workgroup (stream kernel: 4, 8 or 16) */
 } w8a16_plan_t;
+
+/* Plan flags. */
+enum {
+    /* Load A fragments straight into the MFMA register layout instead of
+     * staging coalesced loads through LDS (the weight is always staged). */
+    W8A16_FLAG_DIRECT = 1u
+};
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no
  * GPU call.  Returns W8A16_OK or the first failing check's code. */

@@ -102,7 +102,7 @@ def _covers(p: Plan, m, n, k):
 def test_default_plans_cover_the_problem(m, n, k):
     p = w8.plan(m, n, k)
     _covers(p, m, n, k)
-    assert p.block in (256,)
+    assert p.block in (256, 512, 1024)
     assert p.lds_bytes <= 160 * 1024
     if p.splits > 1:
         assert p.workspace_bytes == p.grid * p.m_blocks * p.n_blocks * 1024
@@ -116,7 +116,14 @@ def test_small_m_plans_stream_kernel_and_fill_the_chip():
         p = w8.plan(m, n, k)
         assert p.kernel == w8.KERNEL_STREAM
         assert p.m_blocks == (1 if m <= 16 else 2)
-        assert p.grid >= 256
+        assert p.grid >= 192          # at least three quarters of the 256 CUs
+        assert p.splits == 1
+
+
+def test_split_k_only_when_tiles_leave_cus_idle():
+    p = w8.plan(1, 128, 65536)
+    assert p.splits > 1 and p.grid <= 256
+    _covers(p, 1, 128, 65536)
 
 
 def test_explicit_plans():
@@ -126,6 +133,12 @@ def test_explicit_plans():
     p = w8.make_plan(16, 4096, 128 * 33, w8.KERNEL_STREAM, 1, 2, 5)
     _covers(p, 16, 4096, 128 * 33)
     assert (p.splits, p.steps_per_split) == (5, 7)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 1, depth=3)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 1, flags=2)
+    p = w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 1, depth=4, flags=w8.FLAG_DIRECT)
+    assert (p.depth, p.flags) == (4, w8.FLAG_DIRECT)
     with pytest.raises(w8.W8A16Error) as e:
         w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 3, 4, 1)
     assert e.value.status == w8.ERR_BAD_PLAN

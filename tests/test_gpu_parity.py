@@ -116,7 +116,7 @@ def test_every_finite_e4m3_code_dequantizes_exactly(w8):
     assert np.array_equal(got[nz], want[nz])
     # all 254 finite codes were exercised
     seen = set(codes[np.arange(n)[None, :], pick[:, None]].reshape(-1).tolist())
-    assert len(seen) == 255   # 254 finite codes + the 0 stand-in is code 0 itself
+    assert seen == set(range(256)) - {0x7F, 0xFF}
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 130, 512), (16, 256, 1024),
@@ -128,16 +128,24 @@ def test_exact_data_bit_exact_default_plan(w8, m, n, k):
     check_full(p, g, exact=True)
 
 
-STREAM_SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (2, 8),
-                 (4, 1), (4, 2), (4, 4)]
+STREAM_SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4),
+                 (4, 1), (4, 2)]
 
 
 @pytest.mark.parametrize("mb,nb", STREAM_SHAPES)
-@pytest.mark.parametrize("splits", [1, 3, 8])
-def test_exact_data_every_stream_variant(w8, mb, nb, splits):
-    m, n, k = 16 * mb - 3, 16 * nb * 3 + 5, 1024
-    p = exact_problem(m, n, k, seed=100 * mb + 10 * nb + splits)
-    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits)
+@pytest.mark.parametrize("depth", [1, 2, 4])
+@pytest.mark.parametrize("direct", [0, 1])
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, waves):
+    m, n, k = 16 * mb - 3, 16 * nb * 3 + 5, 1024 if splits == 1 else 128 * 7
+    p = exact_problem(m, n, k, seed=100 * mb + 10 * nb + splits + 1000 * depth + waves)
+    try:
+        plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=depth,
+                            flags=direct, waves=waves)
+    except w8.W8A16Error as e:
+        assert e.status == w8.ERR_BAD_PLAN and "LDS" in str(e)
+        pytest.skip("variant needs more LDS than a CU has")
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
 
@@ -165,10 +173,6 @@ def test_largest_workload_sampled_parity(w8):
     ok = oracle.within_tolerance(got, oc, bound)
     assert ok.all(), np.argwhere(~ok)[:5]
     assert np.isfinite(oracle.bf16_bits_to_f64(g[:p.m, :p.n])).all()
-    # the all-zero weight blocks give exactly zero contributions: columns of
-    # a scale-block row whose every K block is zero do not occur here, so
-    # check instead that rows/cols never read past the problem
-    assert g.shape == (p.m, p.c_row_stride)
 
 
 def test_determinism_and_plans_agree_within_tolerance(w8):
@@ -178,8 +182,11 @@ def test_determinism_and_plans_agree_within_tolerance(w8):
     g2 = run_gpu(w8, p)
     assert np.array_equal(g1, g2)
     check_full(p, g1)
-    for mb, nb, splits in [(2, 1, 1), (2, 4, 4), (2, 8, 16), (4, 2, 2)]:
-        plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_STREAM, mb, nb, splits)
+    for mb, nb, splits, depth, direct, waves in [(2, 1, 1, 1, 0, 4), (2, 4, 4, 2, 1, 8),
+                                                 (2, 2, 16, 4, 0, 4), (4, 2, 2, 2, 1, 16),
+                                                 (2, 1, 3, 4, 1, 16), (2, 2, 1, 1, 1, 16)]:
+        plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_STREAM, mb, nb, splits, depth, direct,
+                            waves)
         g = run_gpu(w8, p, plan)
         check_full(p, g)
         assert np.array_equal(g, run_gpu(w8, p, plan))
