@@ -82,7 +82,7 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
 {
-    return mb == 8 && (nb == 8 || nb == 16);
+    return mb == 8 && (nb == 4 || nb == 8);
 }
 
 int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
@@ -127,15 +127,27 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      p->lds_bytes, kMaxLdsBytes);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-    } else if (p->kernel == W8A16_KERNEL_TILE && kTileKernelBuilt) {
+    } else if (p->kernel == W8A16_KERNEL_TILE) {
         if (!tile_shape_supported(p->m_blocks, p->n_blocks)) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: tile kernel has no (m_blocks=%u, n_blocks=%u) "
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
+        if (p->depth != 2 && p->depth != 3) {
+            snprintf(buf, sizeof buf, "w8a16_plan: tile kernel depth=%u must be 2 or 3",
+                     p->depth);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        if (p->flags != 0 || (p->waves != 0 && p->waves != 4)) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: tile kernel takes no flags and 4 waves (flags=0x%x, waves=%u)",
+                     p->flags, p->waves);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->waves = 4;
         p->block = kTileThreads;
-        p->lds_bytes = tile_lds_bytes(p->n_blocks);
+        p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth);
     } else {
         snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
         return fail(W8A16_ERR_BAD_PLAN, buf);
@@ -149,6 +161,12 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
     // shrink (e.g. 32 steps in 5 splits of 7 -> 5 splits, the last with 4).
     p->steps_per_split = div_up(ksteps, p->splits);
     p->splits = div_up(ksteps, p->steps_per_split);
+    if (p->kernel == W8A16_KERNEL_TILE && p->steps_per_split > kTileMaxSteps) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_plan: tile kernel splits of %u K steps exceed %u; use splits >= %u",
+                 p->steps_per_split, kTileMaxSteps, div_up(ksteps, kTileMaxSteps));
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
     p->m_tiles = div_up(m, 16 * p->m_blocks);
     p->n_tiles = div_up(n, 16 * p->n_blocks);
     uint64_t tiles = (uint64_t)p->m_tiles * p->n_tiles;
@@ -159,7 +177,12 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         return fail(W8A16_ERR_BAD_PLAN, buf);
     }
     p->grid = (uint32_t)grid;
-    if (p->splits > 1) {
+    if (p->splits > 1 && p->kernel == W8A16_KERNEL_TILE) {
+        // whole FP32 tiles per split, added by a second kernel
+        p->workspace_bytes = (uint64_t)p->splits * p->m_tiles * kTileRows *
+                             p->n_tiles * 16 * p->n_blocks * 4;
+        p->counter_count = 0;
+    } else if (p->splits > 1) {
         p->workspace_bytes = grid * (uint64_t)p->m_blocks * p->n_blocks * kAccBytes;
         p->counter_count = (uint32_t)tiles;
     } else {
@@ -182,16 +205,23 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     const uint32_t ksteps = k / kKStep;
     const uint32_t nb16 = div_up(n, 16);
 
-    if (m > 64 && kTileKernelBuilt) {
-        // Large m: 128-row tiles with the dequantized weight tile shared by
-        // all rows; split K only if the tiles alone cannot fill the chip.
+    if (m > 64) {
+        // Large m: 128 x 128 tiles that share each staged weight tile among
+        // all 128 rows.  K is split until the tiles fill the CUs: besides
+        // parallelism, a split cuts the A bytes every CU pulls from L2
+        // (all of A for a full-K tile), which is what bounds the tile.
         p.kernel = W8A16_KERNEL_TILE;
         p.m_blocks = 8;
-        p.n_blocks = 16;
-        uint32_t tiles = div_up(m, 128) * div_up(n, 256);
+        p.n_blocks = 8;
+        p.depth = 3;
+        p.waves = 4;
+        p.flags = 0;
+        const uint32_t tiles = div_up(m, kTileRows) * div_up(n, 128);
         p.splits = 1;
-        while (tiles * p.splits < p.cu_count && ksteps / (p.splits * 2) >= 8)
+        while (tiles * p.splits * 2 <= p.cu_count && ksteps >= 8 * p.splits)
             p.splits *= 2;
+        if (p.splits < div_up(ksteps, kTileMaxSteps))
+            p.splits = div_up(ksteps, kTileMaxSteps);
     } else {
         // Small m: the weight-streaming kernel.  Measured on MI355X, the
         // best plans give each CU about one workgroup tile, enough waves

@@ -17,14 +17,15 @@ constexpr uint32_t kDefaultCUs = 256;            // MI355X
 // kernels' small static __shared__ variables.
 constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 256;
 constexpr uint32_t kTileThreads = 256;           // tile kernel: 4 waves
-constexpr bool kTileKernelBuilt = false;
+constexpr uint32_t kTileRows = 128;              // tile kernel: rows of C per tile
+constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per split (one per lane)
 
-// LDS of the tile kernel for a 128 x (16 * n_blocks) C tile: two buffers of
-// one K step of A (128 rows, BF16) and of the dequantized weight tile
-// (16 * n_blocks rows, BF16), rows padded by 16 bytes.
-constexpr uint32_t tile_lds_bytes(uint32_t n_blocks)
+// LDS of the tile kernel for a 128 x (16 * n_blocks) C tile with `stages`
+// buffers, each one K step of A (128 rows x 256 bytes of BF16) and of the
+// FP8 weight (16 * n_blocks rows x 128 bytes).
+constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t stages)
 {
-    return 2 * (128 + 16 * n_blocks) * (256 + 16);
+    return stages * (kTileRows * 256 + 16 * n_blocks * 128);
 }
 
 int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,

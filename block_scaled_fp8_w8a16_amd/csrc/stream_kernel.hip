@@ -40,90 +40,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "kernels.h"
 
 namespace w8a16 {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr uint32_t kW = 2048;   // LDS bytes of one 16-row weight block per K step
 constexpr uint32_t kA = 4096;   // LDS bytes of one 16-row A block per K step
-
-// Swizzle of the 16-byte chunk index inside a 128-byte weight row: rows
-// r and r^8 differ in the low bit, so the 16 lanes of one ds_read_b128
-// phase (rows 0..15, same logical chunk) hit distinct banks whether the LDS
-// serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ uint32_t wswz(uint32_t r) { return (r & 7u) ^ (r >> 3); }
-
-// Bytes 0,1 (HI = false) or 2,3 (HI = true) of `raw` -> two BF16 in one dword,
-// the lower byte in the lower half.
-template <bool HI>
-__device__ __forceinline__ uint32_t bf16_pair_from_fp8(uint32_t raw)
-{
-    auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, HI);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// 16 FP8 bytes -> two MFMA operands of 8 BF16 (bytes 0..7, bytes 8..15).
-__device__ __forceinline__ void dequant16(u32x4_t raw, bf16x8_t &lo, bf16x8_t &hi)
-{
-    u32x4_t l, h;
-    l.x = bf16_pair_from_fp8<false>(raw.x);
-    l.y = bf16_pair_from_fp8<true>(raw.x);
-    l.z = bf16_pair_from_fp8<false>(raw.y);
-    l.w = bf16_pair_from_fp8<true>(raw.y);
-    h.x = bf16_pair_from_fp8<false>(raw.z);
-    h.y = bf16_pair_from_fp8<true>(raw.z);
-    h.z = bf16_pair_from_fp8<false>(raw.w);
-    h.w = bf16_pair_from_fp8<true>(raw.w);
-    lo = __builtin_bit_cast(bf16x8_t, l);
-    hi = __builtin_bit_cast(bf16x8_t, h);
-}
-
-// Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    __bf16 b = static_cast<__bf16>(f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, b);
-}
-
-// Map the hardware workgroup id to a logical id so that logical ids that
-// are close (the K splits of one tile, then neighbouring tiles) run on the
-// same XCD: workgroups are dispatched round-robin over the 8 XCDs.
-__device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
-{
-    const uint32_t X = 8;
-    const uint32_t q = grid / X, r = grid % X;
-    const uint32_t xcd = bid % X, slot = bid / X;
-    return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-}
-
-// Store four adjacent outputs C[row][col..col+3] (FP32 -> BF16).
-__device__ __forceinline__ void store_c4(const GemmArgs &g, f32x4_t v, uint32_t row,
-                                         uint32_t col)
-{
-    if (row >= g.m || col >= g.n)
-        return;
-    uint16_t *dst = reinterpret_cast<uint16_t *>(g.c) + (size_t)row * g.c_stride + col;
-    uint32_t b0 = f32_to_bf16_bits(v.x), b1 = f32_to_bf16_bits(v.y);
-    uint32_t b2 = f32_to_bf16_bits(v.z), b3 = f32_to_bf16_bits(v.w);
-    if (col + 3 < g.n && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
-        u32x2_t packed;
-        packed.x = b0 | (b1 << 16);
-        packed.y = b2 | (b3 << 16);
-        *reinterpret_cast<u32x2_t *>(dst) = packed;
-    } else {
-        dst[0] = (uint16_t)b0;
-        if (col + 1 < g.n) dst[1] = (uint16_t)b1;
-        if (col + 2 < g.n) dst[2] = (uint16_t)b2;
-        if (col + 3 < g.n) dst[3] = (uint16_t)b3;
-    }
-}
 
 // Sum of the WAVES partial tiles of pair `pi` for one lane, in wave order.
 // All LDS reads are issued before the additions.

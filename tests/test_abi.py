@@ -104,7 +104,12 @@ def test_default_plans_cover_the_problem(m, n, k):
     _covers(p, m, n, k)
     assert p.block in (256, 512, 1024)
     assert p.lds_bytes <= 160 * 1024
-    if p.splits > 1:
+    if p.splits > 1 and p.kernel == w8.KERNEL_TILE:
+        # whole FP32 tiles per split; no arrival counters (second kernel)
+        assert p.workspace_bytes == (p.splits * p.m_tiles * 128 * p.n_tiles * 16 *
+                                     p.n_blocks * 4)
+        assert p.counter_count == 0
+    elif p.splits > 1:
         assert p.workspace_bytes == p.grid * p.m_blocks * p.n_blocks * 1024
         assert p.counter_count == p.m_tiles * p.n_tiles
     else:
@@ -118,6 +123,25 @@ def test_small_m_plans_stream_kernel_and_fill_the_chip():
         assert p.m_blocks == (1 if m <= 16 else 2)
         assert p.grid >= 192          # at least three quarters of the 256 CUs
         assert p.splits == 1
+
+
+def test_large_m_plans_tile_kernel():
+    p = w8.plan(128, 8192, 8192)
+    assert p.kernel == w8.KERNEL_TILE
+    assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (8, 8, 4, 16)
+    assert p.grid == 256 and p.counter_count == 0
+    assert p.workspace_bytes == 4 * 128 * 8192 * 4
+    assert p.lds_bytes == 3 * (128 * 256 + 128 * 128) <= 160 * 1024 - 256
+    # a split may not exceed 64 K steps (one scale per lane)
+    p = w8.plan(100, 256, 128 * 200)
+    assert p.steps_per_split <= 64
+    _covers(p, 100, 256, 128 * 200)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(100, 256, 128 * 200, w8.KERNEL_TILE, 8, 8, 1, depth=3, waves=4)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=4, waves=4)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 4, 8, 1, depth=3, waves=4)
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():

@@ -150,6 +150,31 @@ def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, wave
     check_full(p, g, exact=True)
 
 
+TILE_VARIANTS = [(nb, depth) for nb in (4, 8) for depth in (2, 3)]
+
+
+@pytest.mark.parametrize("nb,depth", TILE_VARIANTS)
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("m", [65, 128, 200])
+def test_exact_data_every_tile_variant(w8, nb, depth, splits, m):
+    n, k = 16 * nb * 3 + 7, 128 * 7
+    p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, nb, splits, depth=depth, flags=0, waves=4)
+    g = run_gpu(w8, p, plan)
+    check_full(p, g, exact=True)
+
+
+def test_tile_kernel_long_k_and_strides(w8):
+    p = datagen.make_problem(130, 300, 128 * 40, seed=21, a_row_stride=128 * 40 + 24,
+                             c_row_stride=311, c_extra_rows=2)
+    for nb, depth, splits in [(8, 3, 1), (8, 3, 4), (4, 2, 5)]:
+        plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_TILE, 8, nb, splits, depth=depth,
+                            flags=0, waves=4)
+        g = run_gpu(w8, p, plan)
+        check_full(p, g)
+        assert np.array_equal(g, run_gpu(w8, p, plan))
+
+
 # ------------------------------------------------------------- workloads
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3])
