@@ -134,9 +134,13 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->depth != 2 && p->depth != 3) {
-            snprintf(buf, sizeof buf, "w8a16_plan: tile kernel depth=%u must be 2 or 3",
-                     p->depth);
+        const bool depth_ok = p->n_blocks == 8
+                                  ? (p->depth >= 3 && p->depth <= 5)
+                                  : (p->depth == 4 || p->depth == 6 || p->depth == 8);
+        if (!depth_ok) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: tile kernel has no depth=%u variant for n_blocks=%u",
+                     p->depth, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         if (p->flags != 0 || (p->waves != 0 && p->waves != 4)) {
@@ -213,7 +217,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.kernel = W8A16_KERNEL_TILE;
         p.m_blocks = 8;
         p.n_blocks = 8;
-        p.depth = 3;
+        p.depth = 5;
         p.waves = 4;
         p.flags = 0;
         const uint32_t tiles = div_up(m, kTileRows) * div_up(n, 128);

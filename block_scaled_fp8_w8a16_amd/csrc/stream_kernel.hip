@@ -17,7 +17,8 @@
 //   * Per K step a wave loads its weight rows (8 lanes per 128-byte row
 //     segment) and the A rows (16 lanes per 256-byte row segment) into
 //     registers, writes them to its private LDS area in an XOR-swizzled
-//     layout, and reads them back in the 16x16x32 BF16 MFMA operand layout.
+//     layout of 128-byte rows (A as two planes of half rows), and reads them
+//     back in the 16x16x32 BF16 MFMA operand layout without bank conflicts.
 //     The next step's loads are issued before the current step's math.
 //   * The weight is the MFMA's first operand (its 16 rows are 16 columns of
 //     C), A is the second; lane l then holds C[m = l%16][n = 4(l/16)..+3],
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
     for (int q = 0; q < 4; ++q) {
         const uint32_t r = DIRECT ? rr : 4u * q + (lane >> 4);
         if (!DIRECT)
-            adst[q] = r * 256u + (((lane & 15u) ^ r) * 16u);
+            adst[q] = ((lane & 15u) >> 3) * 2048u + r * 128u + (((lane & 7u) ^ wswz(r)) * 16u);
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
             const uint32_t row = m0 + 16u * b + r;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
     uint32_t ard[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        ard[q] = rr * 256u + (((4u * gq + q) ^ rr) * 16u);
+        ard[q] = ((4u * gq + q) >> 3) * 2048u + rr * 128u + ((((4u * gq + q) & 7u) ^ wswz(rr)) * 16u);
     // Scale row of each weight block (a 16-row block never straddles two
     // 128-row scale blocks).
     const float *srow[NBW];

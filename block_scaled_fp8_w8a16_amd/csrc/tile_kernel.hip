@@ -13,10 +13,12 @@
 //     4 x NT/32 MFMA 16x16x32 tiles.
 //   * Per K step the workgroup stages A (128 rows x 256 bytes of BF16) and
 //     the weight (NT rows x 128 bytes of FP8) straight from global memory
-//     into LDS with global_load_lds_dwordx4, in a ring of STAGES buffers.
+//     into LDS with global_load_lds_dwordx4: the weight in a ring of WST
+//     buffers (WST - 1 steps ahead, to cover HBM latency), A in two buffers
+//     (one step ahead; it comes from L2).
 //     Each lane picks the 16 bytes it moves so that the LDS image comes out
-//     XOR-swizzled (conflict-free MFMA operand reads) while every group of
-//     lanes still reads whole 128-byte lines.  The compiler does not track
+//     XOR-swizzled in 128-byte rows (conflict-free MFMA operand reads) while
+//     every 8 lanes still read one whole 128-byte line.  The compiler does not track
 //     these DMA writes, so the kernel waits for them itself (s_waitcnt
 //     vmcnt) and a workgroup barrier per step publishes them and retires
 //     the buffer being refilled.
@@ -69,34 +71,39 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// DMA one K step (A and weight) of this wave's share into LDS stage buffer
-// `sb`.  A __device__ function rather than a lambda: a lambda in a kernel is
+// DMA one K step of A, or of the weight, of this wave's share into an LDS
+// buffer.  __device__ functions rather than lambdas: a lambda in a kernel is
 // also compiled for the host, where the DMA builtin does not exist.
-template <int NA, int NW>
-__device__ __forceinline__ void issue_step(uint8_t *sb, uint32_t wave, uint32_t t,
-                                           const uint8_t *const *asrc,
-                                           const uint8_t *const *wsrc)
+template <int NA>
+__device__ __forceinline__ void issue_a(uint8_t *dst, uint32_t wave, uint32_t t,
+                                        const uint8_t *const *asrc)
 {
 #pragma unroll
     for (int u = 0; u < NA; ++u)
         __builtin_amdgcn_global_load_lds(asrc[u] + t * 256u,
-                                         (lds_void_t *)(sb + (wave * NA + u) * 1024u), 16, 0, 0);
+                                         (lds_void_t *)(dst + (wave * NA + u) * 1024u), 16, 0, 0);
+}
+
+template <int NW>
+__device__ __forceinline__ void issue_w(uint8_t *dst, uint32_t wave, uint32_t t,
+                                        const uint8_t *const *wsrc)
+{
 #pragma unroll
     for (int u = 0; u < NW; ++u)
         __builtin_amdgcn_global_load_lds(wsrc[u] + t * 128u,
-                                         (lds_void_t *)(sb + kABytes + (wave * NW + u) * 1024u),
-                                         16, 0, 0);
+                                         (lds_void_t *)(dst + (wave * NW + u) * 1024u), 16, 0, 0);
 }
 
-template <int NT, int STAGES>
+template <int NT, int WST>
 __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr uint32_t kWBytes = NT * 128;
-    constexpr uint32_t kStage = kABytes + kWBytes;
     constexpr int NA = kABytes / 1024 / 4;   // A DMA instructions per wave per step
     constexpr int NW = kWBytes / 1024 / 4;   // weight DMA instructions per wave per step
-    constexpr int PER_STEP = NA + NW;
+    // LDS: two A buffers, then WST weight buffers.
+    uint8_t *const abuf = lds;
+    uint8_t *const wbuf = lds + 2 * kABytes;
     constexpr int NBW = NT / 32;             // 16-column blocks per wave
     static_assert(NW >= 1 && NBW >= 1, "tile too small");
 
@@ -114,23 +121,28 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     const uint32_t s0 = split * g.steps_per_split;
     const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
 
-    // ---- DMA sources: lane s of A instruction i fills LDS slot s of rows
-    // 4i..4i+3 (16 slots of 16 bytes per 256-byte row); slot p of row r holds
-    // chunk p ^ (r % 16).  Weight instruction i covers rows 8i..8i+7 (8 slots
-    // per 128-byte row); slot p of row r holds chunk p ^ wswz(r % 16).
+    // ---- DMA sources.  In LDS, A is two planes (K-step bytes 0..127 and
+    // 128..255 of each row), each 128 rows x 128 bytes; the weight is NT rows
+    // x 128 bytes.  Within a 128-byte row r, slot p holds 16-byte chunk
+    // p ^ wswz(r % 16): with rows 128 bytes apart this makes the MFMA operand
+    // reads below (16 lanes = 16 consecutive rows, one chunk each) free of
+    // LDS bank conflicts on gfx950, which 256-byte rows are not.  A DMA
+    // instruction fills 1 KiB of LDS = 8 rows of one plane; lane s writes
+    // slot s % 8 of row s / 8, so it reads the chunk that slot holds.
     const uint8_t *asrc[NA];
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
-        const uint32_t i = wave * NA + u;
-        const uint32_t r = 4u * i + (lane >> 4);
-        const uint32_t c = (lane & 15u) ^ (r & 15u);
+        const uint32_t i = wave * NA + u;          // 0..31: plane i / 16, rows 8(i % 16)..+7
+        const uint32_t plane = i >> 4;
+        const uint32_t r = 8u * (i & 15u) + (lane >> 3);
+        const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
         const uint32_t row = min(m0 + r, g.m - 1u);
         asrc[u] = g.a + (size_t)row * g.a_stride * 2u + c * 16u;
     }
     const uint8_t *wsrc[NW];
 #pragma unroll
     for (int u = 0; u < NW; ++u) {
-        const uint32_t i = wave * NW + u;
+        const uint32_t i = wave * NW + u;          // rows 8i..8i+7
         const uint32_t r = 8u * i + (lane >> 3);
         const uint32_t c = (lane & 7u) ^ wswz(r & 15u);
         const uint32_t row = min(n0 + r, g.n - 1u);
@@ -145,13 +157,14 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            aoff[b][q] = (64u * wm + 16u * b + rr) * 256u + (((4u * gq + q) ^ rr) * 16u);
+            aoff[b][q] = ((4u * gq + q) >> 3) * (kTileM * 128u) + (64u * wm + 16u * b + rr) * 128u +
+                         ((((4u * gq + q) & 7u) ^ wswz(rr)) * 16u);
     uint32_t woff[NBW][2];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            woff[j][h] = kABytes + ((NT / 2) * wn + 16u * j + rr) * 128u +
+            woff[j][h] = ((NT / 2) * wn + 16u * j + rr) * 128u +
                          (((2u * gq + h) ^ wswz(rr)) * 16u);
     // Scales of the tile's 128-row block for this split's steps (at most 64,
     // which the planner guarantees), one per lane: lane l holds step s0 + l.
@@ -168,30 +181,36 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
         for (int b = 0; b < 4; ++b)
             acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // Issue order, also in the prologue: iteration i issues A(i + 1), then
+    // W(i + WST - 1).  The weight (from HBM) runs WST - 1 steps ahead, A (from
+    // L2) one step ahead.
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
+    for (int st = 0; st < WST - 2; ++st)
         if (s0 + st < s1)
-            issue_step<NA, NW>(lds + st * kStage, wave, s0 + st, asrc, wsrc);
+            issue_w<NW>(wbuf + st * kWBytes, wave, s0 + st, wsrc);
+    if (s0 < s1)
+        issue_a<NA>(abuf, wave, s0, asrc);
+    if (s0 + WST - 2 < s1)
+        issue_w<NW>(wbuf + (WST - 2) * kWBytes, wave, s0 + WST - 2, wsrc);
 
     for (uint32_t t = s0; t < s1; ++t) {
         const uint32_t idx = t - s0;
-        // This wave's DMA for step t is done once at most the later steps'
-        // groups (up to STAGES-2 of them) are still outstanding.
-        const uint32_t later = min((uint32_t)(STAGES - 2), s1 - 1u - t);
-        if (STAGES >= 3 && later >= 1) {
-            if (STAGES >= 4 && later >= 2)
-                wait_vm<(STAGES >= 4 ? 2 : 0) * PER_STEP>();
-            else
-                wait_vm<(STAGES >= 3 ? 1 : 0) * PER_STEP>();
-        } else {
+        // A(t) was issued one iteration ago, followed only by W(t + WST - 2)
+        // (when that step exists); W(t) was issued before A(t).  So this
+        // wave's DMA for step t is complete once at most that weight group is
+        // outstanding.
+        if (t + WST - 2 < s1)
+            wait_vm<NW>();
+        else
             wait_vm<0>();
-        }
         barrier_lds();
-        if (t + STAGES - 1 < s1)
-            issue_step<NA, NW>(lds + ((idx + STAGES - 1) % STAGES) * kStage, wave,
-                               t + STAGES - 1, asrc, wsrc);
+        if (t + 1 < s1)
+            issue_a<NA>(abuf + ((idx + 1) & 1u) * kABytes, wave, t + 1, asrc);
+        if (t + WST - 1 < s1)
+            issue_w<NW>(wbuf + ((idx + WST - 1) % WST) * kWBytes, wave, t + WST - 1, wsrc);
 
-        const uint8_t *sb = lds + (idx % STAGES) * kStage;
+        const uint8_t *sa = abuf + (idx & 1u) * kABytes;
+        const uint8_t *sw = wbuf + (idx % WST) * kWBytes;
         const float s = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, svec), (int)idx));
         u32x4_t wraw[NBW][2];
@@ -199,14 +218,14 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                wraw[j][h] = *reinterpret_cast<const u32x4_t *>(sb + woff[j][h]);
+                wraw[j][h] = *reinterpret_cast<const u32x4_t *>(sw + woff[j][h]);
         f32x4_t p[NBW][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             bf16x8_t af[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                af[b] = *reinterpret_cast<const bf16x8_t *>(sb + aoff[b][q]);
+                af[b] = *reinterpret_cast<const bf16x8_t *>(sa + aoff[b][q]);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
                 bf16x8_t lo, hi;
@@ -270,10 +289,10 @@ __global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uin
     store_c4(g, s, row, col);
 }
 
-template <int NT, int STAGES>
+template <int NT, int WST>
 hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    auto kern = w8a16_tile_kernel<NT, STAGES>;
+    auto kern = w8a16_tile_kernel<NT, WST>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -301,10 +320,12 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
 hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     switch (p.n_blocks * 10 + p.depth) {
-    case 42: return launch_tile_t<64, 2>(g, p, stream);
-    case 43: return launch_tile_t<64, 3>(g, p, stream);
-    case 82: return launch_tile_t<128, 2>(g, p, stream);
+    case 44: return launch_tile_t<64, 4>(g, p, stream);
+    case 46: return launch_tile_t<64, 6>(g, p, stream);
+    case 48: return launch_tile_t<64, 8>(g, p, stream);
     case 83: return launch_tile_t<128, 3>(g, p, stream);
+    case 84: return launch_tile_t<128, 4>(g, p, stream);
+    case 85: return launch_tile_t<128, 5>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

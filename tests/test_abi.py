@@ -131,7 +131,7 @@ def test_large_m_plans_tile_kernel():
     assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (8, 8, 4, 16)
     assert p.grid == 256 and p.counter_count == 0
     assert p.workspace_bytes == 4 * 128 * 8192 * 4
-    assert p.lds_bytes == 3 * (128 * 256 + 128 * 128) <= 160 * 1024 - 256
+    assert p.lds_bytes == 2 * 128 * 256 + p.depth * 128 * 128 <= 160 * 1024 - 256
     # a split may not exceed 64 K steps (one scale per lane)
     p = w8.plan(100, 256, 128 * 200)
     assert p.steps_per_split <= 64
@@ -139,7 +139,9 @@ def test_large_m_plans_tile_kernel():
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(100, 256, 128 * 200, w8.KERNEL_TILE, 8, 8, 1, depth=3, waves=4)
     with pytest.raises(w8.W8A16Error):
-        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=4, waves=4)
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=6, waves=4)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 4, 1, depth=5, waves=4)
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 4, 8, 1, depth=3, waves=4)
 

@@ -150,7 +150,7 @@ def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, wave
     check_full(p, g, exact=True)
 
 
-TILE_VARIANTS = [(nb, depth) for nb in (4, 8) for depth in (2, 3)]
+TILE_VARIANTS = [(8, 3), (8, 4), (8, 5), (4, 4), (4, 6), (4, 8)]
 
 
 @pytest.mark.parametrize("nb,depth", TILE_VARIANTS)
@@ -167,7 +167,7 @@ def test_exact_data_every_tile_variant(w8, nb, depth, splits, m):
 def test_tile_kernel_long_k_and_strides(w8):
     p = datagen.make_problem(130, 300, 128 * 40, seed=21, a_row_stride=128 * 40 + 24,
                              c_row_stride=311, c_extra_rows=2)
-    for nb, depth, splits in [(8, 3, 1), (8, 3, 4), (4, 2, 5)]:
+    for nb, depth, splits in [(8, 5, 1), (8, 3, 4), (4, 6, 5)]:
         plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_TILE, 8, nb, splits, depth=depth,
                             flags=0, waves=4)
         g = run_gpu(w8, p, plan)
