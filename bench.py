@@ -1,18 +1,23 @@
 """Benchmark of the block-scaled FP8 W8A16 GEMM on one MI355X.
 
 One step = one GEMM call (the whole path: plan, weight stream, dequant,
-MFMA, scale fold, split-K fix-up, BF16 store) on one batch of synthetic
+MFMA, scale fold, K-split reduction, BF16 store) on one batch of synthetic
 input already resident in HBM.  The headline workload is M=8, N=4096,
 K=4096 (FP8 weight, BF16 activations); the other workloads are reported
 alongside in ``all_workloads``.
 
 Weights are measured cold: every call reads a different replica of the
 operands from an arena of >= 512 MiB (twice the 256 MiB Infinity Cache), so
-the weight bytes come from HBM.  Time is taken with HIP events on the stream
-the kernels run on, bracketed by device synchronisation.
+the weight bytes come from HBM.  The K timed calls are captured once into a
+HIP graph and replayed, so the host's per-call launch cost (about 3 us from
+Python) cannot starve the GPU between kernels; time is taken with HIP events
+on the stream the kernels run on, bracketed by device synchronisation.  The
+same calls issued one by one (eager) are timed too and reported beside it.
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only-main]
+    python bench.py --traffic-run          (workload for rocprofv3 --pmc runs)
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 
 from __future__ import annotations
@@ -71,34 +76,44 @@ class Arena:
 
 def time_workload(torch, w8, prob, steps: int, warmup: int, cold: bool = True,
                   plan=None):
+    """Returns (arena, graph ms per call, eager ms per call, replicas)."""
     per_replica = (prob.a.nbytes + prob.w.nbytes + prob.scale.nbytes + prob.c.nbytes)
     replicas = max(1, -(-ARENA_BYTES // per_replica)) if cold else 1
     arena = Arena(torch, prob, replicas)
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
+    stream = torch.cuda.Stream()
     lib_args = (prob.a_row_stride, prob.c_row_stride, prob.m, prob.n, prob.k)
 
     def call(i):
         a, w, s, c = arena.ptrs[i % replicas]
         st = w8.gemm_raw(a, lib_args[0], w, s, c, lib_args[1], lib_args[2], lib_args[3],
-                         lib_args[4], sp, plan)
+                         lib_args[4], stream.cuda_stream, plan)
         if st != 0:
             raise RuntimeError("w8a16_gemm failed: %d %s" % (st, w8.last_error()))
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        call(warmup + i)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop)
-    return arena, ms / steps, wall, replicas
+    with torch.cuda.stream(stream):
+        for i in range(warmup):          # also allocates any K-split workspace
+            call(i)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            call(warmup + i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = start.elapsed_time(stop) / steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                call(warmup + i)
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(stop) / steps
+    return arena, graph_ms, eager_ms, replicas
 
 
 def check_arena_output(arena, oracle, datagen, torch):
@@ -149,7 +164,154 @@ def load_traffic(workload: str, kernel_hash: str):
         return None
 
 
+COPY_BYTES = 256 << 20
+
+
+def traffic_run(wl_name: str):
+    """A short run for rocprofv3 --pmc: 20 cold calls of the workload, then
+    three plain device copies of COPY_BYTES (the counters' calibration)."""
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    wl = datagen.workload(wl_name)
+    prob = datagen.make_workload(wl)
+    per = prob.a.nbytes + prob.w.nbytes + prob.scale.nbytes + prob.c.nbytes
+    replicas = max(1, -(-ARENA_BYTES // per))
+    arena = Arena(torch, prob, replicas)
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(20):
+        a, w, s, c = arena.ptrs[i % replicas]
+        st = w8.gemm_raw(a, prob.a_row_stride, w, s, c, prob.c_row_stride, prob.m, prob.n,
+                         prob.k, sp)
+        if st != 0:
+            raise RuntimeError(w8.last_error())
+    torch.cuda.synchronize()
+    del arena
+    torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES // 8, dtype=torch.float64, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("traffic run done", flush=True)
+
+
+def _pmc_values(directory: str, counter: str):
+    """Per-dispatch counter values by kernel name, from a rocprofv3 CSV."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, wl_name: str, command: str):
+    """Writes profiles/traffic_<workload>.txt: HBM bytes per launch of the
+    GEMM kernel(s) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for one plain device copy of
+    COPY_BYTES (the largest copy dispatch of the run)."""
+    import datagen
+    wl = datagen.workload(wl_name)
+    fetch = _pmc_values(fetch_dir, "FETCH_SIZE")
+    write = _pmc_values(write_dir, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024.0
+
+    def copy_max(vals):
+        # torch's device-to-device copy_ of a contiguous tensor is a runtime
+        # buffer copy; the arena's replica copies are elementwise kernels
+        best = 0.0
+        for k, v in vals.items():
+            if "copyBuffer" in k:
+                best = max(best, max(v))
+        return best
+
+    cw = copy_max(write)                 # the copy writes exactly what it copies
+    cf = copy_max(fetch)
+    f_scale = copy_kib / cf if cf > 0 else float("nan")
+    w_scale = copy_kib / cw if cw > 0 else float("nan")
+    lines = []
+    total = 0.0
+    kernels = sorted(k for k in fetch if "w8a16" in k)
+    for k in kernels:
+        f = sum(fetch[k]) / len(fetch[k])
+        w = sum(write.get(k, [0.0])) / max(1, len(write.get(k, [])))
+        b = (f * f_scale + w * w_scale) * 1024.0
+        total += b
+        lines.append((k, len(fetch[k]), f, w, b))
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % wl.name)
+    with open(path, "w") as fh:
+        fh.write("# HBM traffic per GEMM call on workload %s, from rocprofv3 PMC counters\n"
+                 % wl.name)
+        fh.write("# commands (run from /tmp with TMPDIR=/tmp):\n#   %s\n" % command)
+        fh.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        fh.write("copy_bytes: %d\n" % COPY_BYTES)
+        fh.write("copy_fetch_kib_raw: %.1f\n" % cf)
+        fh.write("copy_write_kib_raw: %.1f\n" % cw)
+        fh.write("fetch_scale: %.4f\n" % f_scale)
+        fh.write("write_scale: %.4f\n" % w_scale)
+        for k, n, f, w, b in lines:
+            short = k.split("(")[0].replace("void ", "").split("::")[-1]
+            fh.write("kernel %s: dispatches %d, fetch_kib_raw %.1f, write_kib_raw %.1f, "
+                     "hbm_bytes %.0f\n" % (short, n, f, w, b))
+        fh.write("hbm_bytes_per_launch: %.0f\n" % total)
+        fh.write("algorithmic_bytes_per_launch: %d\n" % wl.algorithmic_bytes())
+        fh.write("traffic_over_algorithmic: %.3f\n" % (total / wl.algorithmic_bytes()))
+    print(open(path).read())
+
+
+def summarize_trace(trace_dir: str, wl_name: str, command: str):
+    """Writes profiles/kernel_trace_<workload>.txt from a rocprofv3
+    --kernel-trace --stats run: per-kernel dispatch counts and durations."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as fh:
+            rows.extend(csv.DictReader(fh))
+    by = {}
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        by.setdefault(r["Kernel_Name"], []).append(d)
+    path = os.path.join(ROOT, "profiles", "kernel_trace_%s.txt" % wl_name)
+    with open(path, "w") as fh:
+        fh.write("# rocprofv3 kernel trace of the benchmark on workload %s\n" % wl_name)
+        fh.write("# command (run from /tmp with TMPDIR=/tmp):\n#   %s\n" % command)
+        fh.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        fh.write("# kernel | dispatches | mean_us | median_us | min_us | max_us\n")
+        for k, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            if "w8a16" not in k:
+                continue
+            ds = sorted(ds)
+            short = k.replace("void ", "").replace("w8a16::(anonymous namespace)::", "")
+            fh.write("%s | %d | %.3f | %.3f | %.3f | %.3f\n" % (
+                short, len(ds), sum(ds) / len(ds), ds[len(ds) // 2], ds[0], ds[-1]))
+    print(open(path).read())
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        wl_name = sys.argv[3] if len(sys.argv) > 3 else MAIN_WORKLOAD
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- python3 "
+               "bench.py --steps 50 --warmup 5 --no-cpu --only-main --workload %s ; "
+               "python3 bench.py --summarize-trace TRACE_DIR %s" % (wl_name, wl_name))
+        summarize_trace(sys.argv[2], wl_name, cmd)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-run":
+        traffic_run(sys.argv[2] if len(sys.argv) > 2 else MAIN_WORKLOAD)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-traffic":
+        wl_name = sys.argv[4] if len(sys.argv) > 4 else MAIN_WORKLOAD
+        cmd = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -- python3 "
+               "bench.py --traffic-run %s ; rocprofv3 --pmc WRITE_SIZE --output-format csv "
+               "-d WRITE_DIR -- python3 bench.py --traffic-run %s ; python3 bench.py "
+               "--summarize-traffic FETCH_DIR WRITE_DIR %s" % (wl_name, wl_name, wl_name))
+        summarize_traffic(sys.argv[2], sys.argv[3], wl_name, cmd)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -188,8 +350,8 @@ def main():
     prob = datagen.make_workload(wl)
     plan = w8.plan(wl.m, wl.n, wl.k, torch.cuda.get_device_properties(0).multi_processor_count)
     log("timing %s plan=%s" % (wl.name, plan.as_dict()))
-    arena, ms_call, wall, replicas = time_workload(torch, w8, prob, args.steps, args.warmup,
-                                                   cold=not args.warm)
+    arena, ms_call, eager_ms, replicas = time_workload(torch, w8, prob, args.steps,
+                                                       args.warmup, cold=not args.warm)
     parity_ok = check_arena_output(arena, oracle, datagen, torch)
     del arena
     torch.cuda.empty_cache()
@@ -216,6 +378,8 @@ def main():
                    "seed": wl.seed, "weights": "warm" if args.warm else "cold",
                    "arena_replicas": replicas},
         "us_per_call": round(ms_call * 1e3, 3),
+        "us_per_call_eager": round(eager_ms * 1e3, 3),
+        "timing": "HIP graph of the K calls, replayed; HIP events on the launch stream",
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(wl.flops() / (ms_call * 1e-3) / 1e12, 3),
         "plan": plan.as_dict(),
@@ -240,6 +404,7 @@ def main():
         for other in datagen.WORKLOADS:
             if other.name == wl.name:
                 rows.append({"workload": wl.name, "us_per_call": round(ms_call * 1e3, 3),
+                         "us_per_call_eager": round(eager_ms * 1e3, 3),
                              "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2),
                              "tflops": result["tflops"],
                              "pct_mfma": round(100 * result["tflops"] / BF16_PEAK_TFLOPS, 2),
@@ -249,7 +414,7 @@ def main():
             op = datagen.make_workload(other)
             oplan = w8.plan(other.m, other.n, other.k)
             steps = max(20, min(args.steps, 200))
-            ar, oms, _, orep = time_workload(torch, w8, op, steps, max(5, args.warmup // 2))
+            ar, oms, oeager, orep = time_workload(torch, w8, op, steps, max(5, args.warmup // 2))
             ok = check_arena_output(ar, oracle, datagen, torch)
             del ar
             torch.cuda.empty_cache()
@@ -258,6 +423,7 @@ def main():
             log("%s: %.3f us/call, %.1f GB/s, %.1f TFLOP/s (parity %s)" %
                 (other.name, oms * 1e3, ogbs, otf, ok))
             rows.append({"workload": other.name, "us_per_call": round(oms * 1e3, 3),
+                         "us_per_call_eager": round(oeager * 1e3, 3),
                          "gbs": round(ogbs, 1), "pct_hbm": round(100 * ogbs / HBM_PEAK_GBS, 2),
                          "tflops": round(otf, 3),
                          "pct_mfma": round(100 * otf / BF16_PEAK_TFLOPS, 2),
