@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw8a16.so")
 
-SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_kernel.hip"]
+SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_kernel.hip", "ring_kernel.hip"]
 HEADERS = ["plan.h", "kernels.h", "device_common.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

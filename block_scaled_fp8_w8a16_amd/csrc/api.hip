@@ -145,6 +145,8 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
     g.steps_per_split = plan.steps_per_split;
     if (plan.kernel == W8A16_KERNEL_STREAM)
         e = launch_stream(g, plan, stream);
+    else if (plan.kernel == W8A16_KERNEL_RING)
+        e = launch_ring(g, plan, stream);
     else
         e = launch_tile(g, plan, stream);
     if (e != hipSuccess)

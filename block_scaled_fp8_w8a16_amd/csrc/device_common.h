@@ -45,6 +45,10 @@ __device__ __forceinline__ void dequant16(u32x4_t raw, bf16x8_t &lo, bf16x8_t &h
     hi = __builtin_bit_cast(bf16x8_t, h);
 }
 
+// Step offset between the K walks of consecutive tiles (odd, so tile t
+// starts at step 37t mod span and neighbouring tiles are far apart).
+constexpr uint32_t kRotStride = 37;
+
 // Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 {
@@ -61,6 +65,27 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
     const uint32_t q = grid / X, r = grid % X;
     const uint32_t xcd = bid % X, slot = bid / X;
     return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// LDS pointer type of the global_load_lds builtin (LDS DMA).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone.  The memory clobber
+// keeps LDS reads of the DMA'd data from moving above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that does not drain outstanding global loads (the
+// ordinary __syncthreads() waits for every in-flight DMA step): it waits only
+// for this wave's LDS reads, so no wave can refill a buffer another wave is
+// still reading.  The DMA data of a step is covered by wait_vm() before it.
+__device__ __forceinline__ void barrier_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Store four adjacent outputs C[row][col..col+3] (FP32 -> BF16).

@@ -116,11 +116,37 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->block = p->waves * 64;
+        p->stage_steps = 0;
         const bool direct = (p->flags & W8A16_FLAG_DIRECT) != 0;
         uint32_t per_wave = p->n_blocks * kWBlockBytes + (direct ? 0u : p->m_blocks * kABlockBytes);
         uint32_t staging = p->waves * per_wave;
         uint32_t reduce = p->waves * p->n_blocks * p->m_blocks * kAccBytes;
         p->lds_bytes = staging > reduce ? staging : reduce;
+        if (p->lds_bytes > kMaxLdsBytes) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
+                     p->lds_bytes, kMaxLdsBytes);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+    } else if (p->kernel == W8A16_KERNEL_RING) {
+        // m <= 8 stages 8 A rows; the flag is derived, not chosen
+        const bool a8 = m <= 8 && p->m_blocks == 1;
+        p->flags = a8 ? (uint32_t)W8A16_FLAG_A8 : 0u;
+        if (!ring_shape_ok(p->m_blocks, p->n_blocks, p->stage_steps, p->depth, p->waves, a8)) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: ring kernel has no (m_blocks=%u, n_blocks=%u, stage_steps=%u, "
+                     "depth=%u, waves=%u) variant", p->m_blocks, p->n_blocks, p->stage_steps,
+                     p->depth, p->waves);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        if (ksteps > p->waves * 64u || p->splits != 1) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: ring kernel needs K/128=%u at most %u and splits=1 (got %u)",
+                     ksteps, p->waves * 64u, p->splits);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->block = p->waves * 64;
+        p->lds_bytes = ring_lds_bytes(p->m_blocks, p->n_blocks, p->stage_steps, p->depth, a8, ksteps);
         if (p->lds_bytes > kMaxLdsBytes) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
@@ -150,6 +176,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->waves = 4;
+        p->stage_steps = 0;
         p->block = kTileThreads;
         p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth);
     } else {
@@ -261,6 +288,35 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.splits = 1;
         while (tiles * p.splits * 2 <= p.cu_count && ksteps >= 4 * p.waves * p.splits)
             p.splits *= 2;
+
+        // A large weight (>= 48 MiB) with 8..32 rows streams faster through
+        // the ring kernel's row-contiguous LDS-DMA stages (measured 3-9 %);
+        // below that, or with fewer rows, its slower start does not pay off.
+        const uint64_t wbytes = (uint64_t)n * k;
+        const uint32_t rmb = m <= 16 ? 1 : 2;
+        if (m >= 8 && m <= 32 && wbytes >= (48ull << 20) && p.splits == 1) {
+            const bool a8 = m <= 8;
+            // 16 waves measured best for 16 rows x 64 columns, else 8; three
+            // stages in flight unless LDS allows only two.
+            const uint32_t wcand[2] = {(rmb == 1 && nbw == 4) ? 16u : 8u,
+                                       (rmb == 1 && nbw == 4) ? 8u : 16u};
+            bool chosen = false;
+            for (uint32_t wi = 0; wi < 2 && !chosen; ++wi) {
+                for (uint32_t depth = 3; depth >= 2 && !chosen; --depth) {
+                    const uint32_t rw = wcand[wi];
+                    if (!ring_shape_ok(rmb, nbw, 4, depth, rw, a8) || ksteps > rw * 64u ||
+                        ring_lds_bytes(rmb, nbw, 4, depth, a8, ksteps) > kMaxLdsBytes)
+                        continue;
+                    p.kernel = W8A16_KERNEL_RING;
+                    p.m_blocks = rmb;
+                    p.n_blocks = nbw;
+                    p.stage_steps = 4;
+                    p.depth = depth;
+                    p.waves = rw;
+                    chosen = true;
+                }
+            }
+        }
     }
     st = plan_finalize(m, n, k, &p);
     if (st != W8A16_OK)

@@ -28,6 +28,46 @@ constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t stages)
     return 2 * kTileRows * 256 + stages * 16 * n_blocks * 128;
 }
 
+// Ring kernel geometry, shared by the planner and the kernel dispatch.  A
+// workgroup owns nbw 16-column blocks and mb 16-row blocks of C (a8: m <= 8,
+// only 8 A rows staged) over all of K, in stages of sk K steps; a ring of
+// nst stages is in flight.  One stage holds 16 * nbw weight rows x sk * 128
+// bytes and the A rows x sk * 256 bytes.
+constexpr uint32_t ring_a_rows(uint32_t mb, bool a8) { return a8 ? 8 : 16 * mb; }
+
+constexpr uint32_t ring_stage_bytes(uint32_t mb, uint32_t nbw, uint32_t sk, bool a8)
+{
+    return sk * (16 * nbw * 128 + ring_a_rows(mb, a8) * 256);
+}
+
+// LDS of the ring kernel: the ring plus the tile's scale row (K/128 floats,
+// loaded 64 at a time).
+constexpr uint32_t ring_lds_bytes(uint32_t mb, uint32_t nbw, uint32_t sk, uint32_t nst, bool a8,
+                                  uint32_t ksteps)
+{
+    return nst * ring_stage_bytes(mb, nbw, sk, a8) + (ksteps + 63) / 64 * 256;
+}
+
+// Shapes the ring kernel is built for: every stage splits evenly into 1 KiB
+// DMA loads over the waves, the waves split evenly over the column blocks,
+// the ring fits in LDS (with room for a small scale row) and can hold the
+// waves' partial tiles at the end.
+constexpr bool ring_shape_ok(uint32_t mb, uint32_t nbw, uint32_t sk, uint32_t nst, uint32_t waves,
+                             bool a8)
+{
+    const bool mb_ok = mb == 1 || mb == 2;
+    const bool nb_ok = nbw == 1 || nbw == 2 || nbw == 4;
+    const bool sk_ok = sk == 4 || sk == 8;
+    const bool nst_ok = nst >= 2 && nst <= 4;
+    const bool w_ok = waves == 8 || waves == 16;
+    if (!(mb_ok && nb_ok && sk_ok && nst_ok && w_ok) || (a8 && mb != 1))
+        return false;
+    const uint32_t loads = (16 * nbw * sk * 128 + ring_a_rows(mb, a8) * sk * 256) / 1024;
+    const uint32_t ring = nst * ring_stage_bytes(mb, nbw, sk, a8);
+    return waves % nbw == 0 && loads % waves == 0 && ring + 1024 <= kMaxLdsBytes &&
+           waves * mb * 1024 <= ring;
+}
+
 int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
                uint32_t c_row_stride);
 int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);

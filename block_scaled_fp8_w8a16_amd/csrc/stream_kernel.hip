@@ -29,6 +29,11 @@
 //     contiguous weight bytes and 64 contiguous A bytes.
 //   * FP8 -> BF16 with v_cvt_scalef32_pk_bf16_fp8 (scale 1.0): every E4M3
 //     value, subnormals included, is a BF16 value, so the dequant is exact.
+//   * Each workgroup starts its walk over its K range at a tile-dependent
+//     offset and wraps around.  With a power-of-two K, workgroups that all
+//     start at k = 0 send every concurrent request to the same few HBM
+//     channels; rotated starts spread them.  The order of the scale-folded
+//     step partials in each wave's accumulator changes; the set does not.
 //   * Each step's 16x16 MFMA partial starts from zero and is folded into
 //     the FP32 accumulator as acc = fma(scale, partial, acc).
 //   * The 4 waves' accumulators are added in LDS in wave order.  With K
@@ -88,9 +93,17 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
     const uint32_t ksteps = g.k / 128u;
     const uint32_t s0 = split * g.steps_per_split;
     const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
-    // This wave's K steps: first, first + 4, first + 8, ... (nw of them).
+    // This wave's K steps: first, first + WAVES, ... (nw of them), each
+    // mapped to physical step s0 + (i - s0 + rot) mod span.
     const uint32_t first = s0 + wave;
     const uint32_t nw = first < s1 ? (s1 - first + WAVES - 1) / WAVES : 0u;
+    const uint32_t span = s1 - s0;
+    const uint32_t rot = span ? (tile * kRotStride) % span : 0u;
+    auto phys = [&](uint32_t i) {
+        uint32_t x = i - s0 + rot;
+        x = x >= span ? x - span : x;
+        return s0 + x;
+    };
 
     uint8_t *wl = lds + wave * (NBW * kW + (DIRECT ? 0u : MB * kA));
     uint8_t *al = wl + NBW * kW;
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
         if ((uint32_t)d < nw)
-            issue(d, first + WAVES * d);
+            issue(d, phys(first + WAVES * d));
 
     for (uint32_t base = 0; base < nw; base += DEPTH) {
 #pragma unroll
@@ -217,7 +230,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
                         *reinterpret_cast<u32x4_t *>(al + b * kA + adst[q]) = ca[b][q];
             }
             if (i + DEPTH < nw)
-                issue(d, first + WAVES * (i + DEPTH));
+                issue(d, phys(first + WAVES * (i + DEPTH)));
 
             bf16x8_t af[MB][4];
 #pragma unroll

@@ -48,28 +48,8 @@ namespace {
 
 using namespace dev;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 constexpr uint32_t kTileM = 128;
 constexpr uint32_t kABytes = kTileM * 256;   // one K step of A in LDS
-
-// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone.  The memory clobber
-// keeps LDS reads of the DMA'd data from moving above the wait.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier that does not drain outstanding global loads (the
-// ordinary __syncthreads() waits for every in-flight DMA step): it waits only
-// for this wave's LDS reads, so no wave can refill a buffer another wave is
-// still reading.  The DMA data of a step is covered by wait_vm() before it.
-__device__ __forceinline__ void barrier_lds()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // DMA one K step of A, or of the weight, of this wave's share into an LDS
 // buffer.  __device__ functions rather than lambdas: a lambda in a kernel is
@@ -120,6 +100,16 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     const uint32_t ksteps = g.k / 128u;
     const uint32_t s0 = split * g.steps_per_split;
     const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
+    // Logical step t of the split is physical step s0 + (t - s0 + rot) mod
+    // span: tiles start their K walks at different offsets, which spreads
+    // concurrent weight reads over the HBM channels for power-of-two K.
+    const uint32_t span = s1 - s0;
+    const uint32_t rot = span ? (tile * kRotStride) % span : 0u;
+    auto phys = [&](uint32_t t) {
+        uint32_t x = t - s0 + rot;
+        x = x >= span ? x - span : x;
+        return s0 + x;
+    };
 
     // ---- DMA sources.  In LDS, A is two planes (K-step bytes 0..127 and
     // 128..255 of each row), each 128 rows x 128 bytes; the weight is NT rows
@@ -187,11 +177,11 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
 #pragma unroll
     for (int st = 0; st < WST - 2; ++st)
         if (s0 + st < s1)
-            issue_w<NW>(wbuf + st * kWBytes, wave, s0 + st, wsrc);
+            issue_w<NW>(wbuf + st * kWBytes, wave, phys(s0 + st), wsrc);
     if (s0 < s1)
-        issue_a<NA>(abuf, wave, s0, asrc);
+        issue_a<NA>(abuf, wave, phys(s0), asrc);
     if (s0 + WST - 2 < s1)
-        issue_w<NW>(wbuf + (WST - 2) * kWBytes, wave, s0 + WST - 2, wsrc);
+        issue_w<NW>(wbuf + (WST - 2) * kWBytes, wave, phys(s0 + WST - 2), wsrc);
 
     for (uint32_t t = s0; t < s1; ++t) {
         const uint32_t idx = t - s0;
@@ -205,14 +195,14 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
             wait_vm<0>();
         barrier_lds();
         if (t + 1 < s1)
-            issue_a<NA>(abuf + ((idx + 1) & 1u) * kABytes, wave, t + 1, asrc);
+            issue_a<NA>(abuf + ((idx + 1) & 1u) * kABytes, wave, phys(t + 1), asrc);
         if (t + WST - 1 < s1)
-            issue_w<NW>(wbuf + ((idx + WST - 1) % WST) * kWBytes, wave, t + WST - 1, wsrc);
+            issue_w<NW>(wbuf + ((idx + WST - 1) % WST) * kWBytes, wave, phys(t + WST - 1), wsrc);
 
         const uint8_t *sa = abuf + (idx & 1u) * kABytes;
         const uint8_t *sw = wbuf + (idx % WST) * kWBytes;
         const float s = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, svec), (int)idx));
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, svec), (int)(phys(t) - s0)));
         u32x4_t wraw[NBW][2];
 #pragma unroll
         for (int j = 0; j < NBW; ++j)

@@ -69,11 +69,17 @@ typedef enum w8a16_kernel {
     /* Tiled kernel for large m: a workgroup owns a 128-row x n_blocks*16
      * column tile of C, shares the A and dequantized W tiles of each K step
      * through LDS, and its waves split the tile, not K. */
-    W8A16_KERNEL_TILE = 2
+    W8A16_KERNEL_TILE = 2,
+    /* Ring kernel for small m: a workgroup owns n_blocks 16-column blocks
+     * and m_blocks 16-row blocks of C over all of K, streams K in stages of
+     * stage_steps steps with a ring of `depth` stages in flight (1 KiB
+     * row-contiguous LDS-DMA loads), and its waves, grouped per column
+     * block, take the stages' steps round-robin.  No K split. */
+    W8A16_KERNEL_RING = 3
 } w8a16_kernel;
 
 /* Launch plan.  w8a16_plan() fills every field; callers may change
- * kernel, m_blocks, n_blocks, splits, depth, flags and waves and pass the result to
+ * kernel, m_blocks, n_blocks, splits, depth, flags, waves and stage_steps and pass the result to
  * w8a16_gemm_planned(), which recomputes the derived fields and rejects a
  * plan the kernels do not support (W8A16_ERR_BAD_PLAN). */
 typedef struct w8a16_plan {
@@ -90,16 +96,22 @@ typedef struct w8a16_plan {
     uint64_t workspace_bytes; /* split-K FP32 partials (derived; 0 if splits == 1) */
     uint32_t counter_count;   /* split-K arrival counters (derived) */
     uint32_t cu_count;        /* compute units the plan was sized for */
-    uint32_t depth;           /* K steps each wave keeps in flight (1, 2 or 4) */
+    uint32_t depth;           /* stream: K steps each wave keeps in flight (1, 2, 4);
+                                 tile: weight ring buffers; ring: stages in flight (2..4) */
     uint32_t flags;           /* W8A16_FLAG_* bits */
-    uint32_t waves;           /* waves per workgroup (stream kernel: 4, 8 or 16) */
+    uint32_t waves;           /* waves per workgroup (stream 4/8/16, ring 8/16, tile 4) */
+    uint32_t stage_steps;     /* ring: K steps per stage (4 or 8); 0 for the others */
 } w8a16_plan_t;
 
 /* Plan flags. */
 enum {
-    /* Load A fragments straight into the MFMA register layout instead of
-     * staging coalesced loads through LDS (the weight is always staged). */
-    W8A16_FLAG_DIRECT = 1u
+    /* Stream kernel: load A fragments straight into the MFMA register
+     * layout instead of staging coalesced loads through LDS (the weight is
+     * always staged). */
+    W8A16_FLAG_DIRECT = 1u,
+    /* Ring kernel, m <= 8 with m_blocks == 1: stage 8 A rows instead of 16
+     * (derived by w8a16_plan_finalize from m; callers need not set it). */
+    W8A16_FLAG_A8 = 2u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

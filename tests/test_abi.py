@@ -116,13 +116,52 @@ def test_default_plans_cover_the_problem(m, n, k):
         assert p.workspace_bytes == 0
 
 
-def test_small_m_plans_stream_kernel_and_fill_the_chip():
-    for m, n, k in [(8, 4096, 4096), (16, 12288, 5120), (32, 6144, 2048)]:
+def test_small_m_plans_fill_the_chip():
+    # weights under 48 MiB stream; 8..32 rows over a larger weight take the
+    # ring kernel
+    for m, n, k, kern in [(8, 4096, 4096, w8.KERNEL_STREAM), (16, 12288, 5120, w8.KERNEL_RING),
+                          (32, 6144, 2048, w8.KERNEL_STREAM), (4, 14336, 4096, w8.KERNEL_STREAM),
+                          (8, 12288, 5120, w8.KERNEL_RING), (32, 8192, 8192, w8.KERNEL_RING)]:
         p = w8.plan(m, n, k)
-        assert p.kernel == w8.KERNEL_STREAM
+        assert p.kernel == kern, (m, n, k)
         assert p.m_blocks == (1 if m <= 16 else 2)
         assert p.grid >= 192          # at least three quarters of the 256 CUs
         assert p.splits == 1
+        if kern == w8.KERNEL_RING:
+            assert p.stage_steps == 4 and p.depth in (2, 3)
+            assert p.flags == (w8.FLAG_A8 if m <= 8 else 0)
+            assert p.lds_bytes <= 160 * 1024 - 256
+        else:
+            assert p.stage_steps == 0
+
+
+def test_ring_plans():
+    p = w8.make_plan(16, 12288, 5120, w8.KERNEL_RING, 1, 4, 1, depth=3, waves=16, stage_steps=4)
+    _covers(p, 16, 12288, 5120)
+    stage = 4 * (64 * 128 + 16 * 256)
+    assert p.lds_bytes == 3 * stage + (40 + 63) // 64 * 256
+    assert p.block == 1024 and p.flags == 0 and p.workspace_bytes == 0
+    # the 8-row A staging is derived from m
+    p = w8.make_plan(5, 300, 1024, w8.KERNEL_RING, 1, 1, 1, depth=4, waves=16, stage_steps=8,
+                     flags=0)
+    assert p.flags == w8.FLAG_A8
+    bad = [dict(splits=2),                                   # no K split
+           dict(stage_steps=6),                              # 4 or 8 steps per stage
+           dict(depth=5),                                    # 2..4 stages
+           dict(waves=4),                                    # 8 or 16 waves
+           dict(n_blocks=4, stage_steps=8, depth=4)]         # ring exceeds LDS
+    for b in bad:
+        args = dict(m_blocks=1, n_blocks=1, splits=1, depth=3, waves=16, stage_steps=4)
+        args.update(b)
+        with pytest.raises(w8.W8A16Error) as e:
+            w8.make_plan(16, 4096, 4096, w8.KERNEL_RING, args["m_blocks"], args["n_blocks"],
+                         args["splits"], depth=args["depth"], waves=args["waves"],
+                         stage_steps=args["stage_steps"])
+        assert e.value.status == w8.ERR_BAD_PLAN, b
+    # K/128 must not exceed the threads (one scale per thread)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(16, 256, 128 * 513, w8.KERNEL_RING, 1, 1, 1, depth=3, waves=8,
+                     stage_steps=4)
 
 
 def test_large_m_plans_tile_kernel():

@@ -72,15 +72,17 @@ def check_full(prob, gpu_c, exact=False):
 
 def exact_problem(m, n, k, seed, a_row_stride=None, c_row_stride=None, c_extra_rows=1):
     """Operands whose products and FP32 sums are exact: A in {-2..2}, weight
-    codes with |value| < 4 (all subnormals included), scales in {1/2, 1, 2},
-    K <= 1024 -- partial sums stay below 2^24 units of 2^-10."""
-    assert k <= 1024
+    codes with |value| < 4 for K <= 1024 and < 1/2 for K <= 8192 (all
+    subnormals included), scales in {1/2, 1, 2} -- every product is a
+    multiple of 2^-10 and every partial sum stays below 2^24 such units."""
+    assert k <= 8192
     rng = np.random.default_rng(seed)
     p = datagen.make_problem(m, n, k, seed, a_row_stride, c_row_stride,
                              c_extra_rows=c_extra_rows)
     a_int = rng.integers(-2, 3, size=(m, k)).astype(np.float32)
     p.a[:, :k] = datagen.to_bf16_bits(a_int)
-    mag = rng.integers(0, 0x50, size=(n, k), dtype=np.uint8)     # e <= 9: |v| < 4
+    top = 0x50 if k <= 1024 else 0x30                             # e <= 9 or e <= 5
+    mag = rng.integers(0, top, size=(n, k), dtype=np.uint8)
     sign = rng.integers(0, 2, size=(n, k), dtype=np.uint8) << 7
     p.w[...] = mag | sign
     p.scale[...] = rng.choice(np.float32([0.5, 1.0, 2.0]), size=p.scale.shape)
@@ -148,6 +150,53 @@ def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, wave
         pytest.skip("variant needs more LDS than a CU has")
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
+
+
+RING_SHAPES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)]
+
+
+@pytest.mark.parametrize("mb,nb", RING_SHAPES)
+@pytest.mark.parametrize("sk", [4, 8])
+@pytest.mark.parametrize("depth", [2, 3, 4])
+@pytest.mark.parametrize("wv", [8, 16])
+@pytest.mark.parametrize("msmall", [False, True])
+def test_exact_data_every_ring_variant(w8, mb, nb, sk, depth, wv, msmall):
+    """More stages than ring slots, a ragged last stage, ragged m and n."""
+    if msmall and mb != 1:
+        pytest.skip("the 8-row A staging applies to one M block")
+    m = 5 if msmall else 16 * mb - 3
+    n, k = 16 * nb * 3 + 5, 128 * (sk * (depth + 1) + 3)
+    try:
+        plan = w8.make_plan(m, n, k, w8.KERNEL_RING, mb, nb, 1, depth=depth, flags=0,
+                            waves=wv, stage_steps=sk)
+    except w8.W8A16Error as e:
+        assert e.status == w8.ERR_BAD_PLAN
+        pytest.skip("no such ring variant: %s" % e)
+    assert plan.flags == (w8.FLAG_A8 if msmall else 0)
+    p = exact_problem(m, n, k, seed=mb * 1000 + nb * 100 + sk * 10 + depth + wv)
+    check_full(p, run_gpu(w8, p, plan), exact=True)
+
+
+def test_ring_kernel_strides_and_short_k(w8):
+    """Pitched A and C, and K shorter than one stage (the whole ring is
+    clamped loads but the first slot)."""
+    for (m, n, k) in [(7, 300, 128 * 20), (16, 200, 128), (30, 100, 128 * 3)]:
+        p = datagen.make_problem(m, n, k, seed=m + n + k, a_row_stride=k + 24,
+                                 c_row_stride=n + 11, c_extra_rows=2)
+        mb = 1 if m <= 16 else 2
+        ran = 0
+        for sk, depth, wv, nb in [(8, 4, 16, 1), (8, 3, 16, 1), (4, 3, 8, 2), (4, 2, 16, 1),
+                                  (4, 3, 16, 2)]:
+            try:
+                plan = w8.make_plan(m, n, k, w8.KERNEL_RING, mb, nb, 1, depth=depth,
+                                    flags=0, waves=wv, stage_steps=sk)
+            except w8.W8A16Error:
+                continue
+            g = run_gpu(w8, p, plan)
+            check_full(p, g)
+            assert np.array_equal(g, run_gpu(w8, p, plan))
+            ran += 1
+        assert ran >= 2
 
 
 TILE_VARIANTS = [(8, 3), (8, 4), (8, 5), (4, 4), (4, 6), (4, 8)]
