@@ -391,8 +391,8 @@ def main():
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "w8a16_stream_kernel" if plan.kernel == w8.KERNEL_STREAM
-                      else "w8a16_tile_kernel",
+            "kernel": {w8.KERNEL_STREAM: "w8a16_stream_kernel", w8.KERNEL_TILE: "w8a16_tile_kernel",
+                       w8.KERNEL_RING: "w8a16_ring_kernel"}.get(plan.kernel, "?"),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
         "kernel_source_hash": khash,

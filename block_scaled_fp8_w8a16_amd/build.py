@@ -25,6 +25,12 @@ ARCH = "gfx950"
 # Packed FP32 ops (v_pk_*_f32) are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# Per-source extras.  The tile kernel folds each K step's MFMA partial into
+# FP32 accumulators with VALU FMAs; with the partials in AGPRs every fold
+# first copies them out (v_accvgpr_read), which measured as the single most
+# expensive part of its loop.  The VGPR form of the MFMA keeps them in VGPRs.
+EXTRA_FLAGS = {"tile_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def build(verbose: bool = False) -> str:
     objs = []
@@ -36,7 +42,7 @@ def build(verbose: bool = False) -> str:
         if src.endswith(".hip"):
             cmd = [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                    "-Wall", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS + \
-                  ["-c", path, "-o", obj]
+                  EXTRA_FLAGS.get(src, []) + ["-c", path, "-o", obj]
         else:
             cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
                    "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]

@@ -160,25 +160,28 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        const bool depth_ok = p->n_blocks == 8
-                                  ? (p->depth >= 3 && p->depth <= 5)
-                                  : (p->depth == 4 || p->depth == 6 || p->depth == 8);
-        if (!depth_ok) {
+        if ((p->flags & ~(uint32_t)W8A16_FLAG_A3) != 0 || (p->waves != 0 && p->waves != 4)) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel has no depth=%u variant for n_blocks=%u",
-                     p->depth, p->n_blocks);
+                     "w8a16_plan: tile kernel takes only the A3 flag and 4 waves "
+                     "(flags=0x%x, waves=%u)", p->flags, p->waves);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->flags != 0 || (p->waves != 0 && p->waves != 4)) {
+        // Built (weight buffers, A buffers) pairs; all fit in LDS.
+        const uint32_t ast = (p->flags & W8A16_FLAG_A3) ? 3u : 2u;
+        const bool depth_ok = p->n_blocks == 8
+                                  ? (ast == 2 ? (p->depth >= 3 && p->depth <= 5) : p->depth == 3)
+                                  : (ast == 2 ? (p->depth == 4 || p->depth == 6 || p->depth == 8)
+                                              : (p->depth == 4 || p->depth == 6));
+        if (!depth_ok) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel takes no flags and 4 waves (flags=0x%x, waves=%u)",
-                     p->flags, p->waves);
+                     "w8a16_plan: tile kernel has no depth=%u variant for n_blocks=%u with %u "
+                     "A buffers", p->depth, p->n_blocks, ast);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->waves = 4;
         p->stage_steps = 0;
         p->block = kTileThreads;
-        p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth);
+        p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth, ast);
     } else {
         snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
         return fail(W8A16_ERR_BAD_PLAN, buf);
@@ -244,7 +247,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.kernel = W8A16_KERNEL_TILE;
         p.m_blocks = 8;
         p.n_blocks = 8;
-        p.depth = 5;
+        p.depth = 3;   // measured best of 3..5 weight buffers at 128 x 8192 x 8192
         p.waves = 4;
         p.flags = 0;
         const uint32_t tiles = div_up(m, kTileRows) * div_up(n, 128);

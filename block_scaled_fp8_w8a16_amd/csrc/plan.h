@@ -20,12 +20,13 @@ constexpr uint32_t kTileThreads = 256;           // tile kernel: 4 waves
 constexpr uint32_t kTileRows = 128;              // tile kernel: rows of C per tile
 constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per split (one per lane)
 
-// LDS of the tile kernel for a 128 x (16 * n_blocks) C tile: two buffers of
-// one K step of A (128 rows x 256 bytes of BF16) and `stages` buffers of one
-// K step of the FP8 weight (16 * n_blocks rows x 128 bytes).
-constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t stages)
+// LDS of the tile kernel for a 128 x (16 * n_blocks) C tile: a_stages
+// buffers of one K step of A (128 rows x 256 bytes of BF16), w_stages
+// buffers of one K step of the FP8 weight (16 * n_blocks rows x 128 bytes)
+// and the split's scale row (at most 64 floats).
+constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t w_stages, uint32_t a_stages)
 {
-    return 2 * kTileRows * 256 + stages * 16 * n_blocks * 128;
+    return a_stages * kTileRows * 256 + w_stages * 16 * n_blocks * 128 + 256;
 }
 
 // Ring kernel geometry, shared by the planner and the kernel dispatch.  A

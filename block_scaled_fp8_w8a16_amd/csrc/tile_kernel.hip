@@ -14,14 +14,20 @@
 //   * Per K step the workgroup stages A (128 rows x 256 bytes of BF16) and
 //     the weight (NT rows x 128 bytes of FP8) straight from global memory
 //     into LDS with global_load_lds_dwordx4: the weight in a ring of WST
-//     buffers (WST - 1 steps ahead, to cover HBM latency), A in two buffers
-//     (one step ahead; it comes from L2).
+//     buffers (WST - 1 steps ahead, to cover HBM latency), A in a ring of
+//     AST buffers (AST - 1 steps ahead; it comes from L2).
 //     Each lane picks the 16 bytes it moves so that the LDS image comes out
 //     XOR-swizzled in 128-byte rows (conflict-free MFMA operand reads) while
 //     every 8 lanes still read one whole 128-byte line.  The compiler does not track
 //     these DMA writes, so the kernel waits for them itself (s_waitcnt
 //     vmcnt) and a workgroup barrier per step publishes them and retires
-//     the buffer being refilled.
+//     the buffers being refilled.
+//   * vmcnt counts a wave's loads in issue order, so a wave that issued both
+//     rings would, waiting for the near A step, also wait for every weight
+//     step issued before it, and the weight ring would in effect be two
+//     steps deep.  Loads are therefore split by wave: the even waves issue
+//     the weight ring, the odd waves the A ring (and the scale row), and
+//     each waits only for its own ring.
 //   * The weight is dequantized after the LDS read (FP8 halves LDS traffic),
 //     exactly, with v_cvt_scalef32_pk_bf16_fp8 at scale 1.0.
 //   * Each step's MFMA partial starts at zero and is folded into the FP32
@@ -52,44 +58,53 @@ constexpr uint32_t kTileM = 128;
 constexpr uint32_t kABytes = kTileM * 256;   // one K step of A in LDS
 
 // DMA one K step of A, or of the weight, of this wave's share into an LDS
-// buffer.  __device__ functions rather than lambdas: a lambda in a kernel is
-// also compiled for the host, where the DMA builtin does not exist.
-template <int NA>
-__device__ __forceinline__ void issue_a(uint8_t *dst, uint32_t wave, uint32_t t,
-                                        const uint8_t *const *asrc)
+// buffer: loads u = 0..N-1 of the wave's group g, each one 1 KiB of LDS.
+// __device__ functions rather than lambdas: a lambda in a kernel is also
+// compiled for the host, where the DMA builtin does not exist.
+template <int N, uint32_t STEP_BYTES>
+__device__ __forceinline__ void issue_ring(uint8_t *dst, uint32_t grp, uint32_t t,
+                                           const uint8_t *const *src)
 {
 #pragma unroll
-    for (int u = 0; u < NA; ++u)
-        __builtin_amdgcn_global_load_lds(asrc[u] + t * 256u,
-                                         (lds_void_t *)(dst + (wave * NA + u) * 1024u), 16, 0, 0);
+    for (int u = 0; u < N; ++u)
+        __builtin_amdgcn_global_load_lds(src[u] + t * STEP_BYTES,
+                                         (lds_void_t *)(dst + (grp * N + u) * 1024u), 16, 0, 0);
 }
 
-template <int NW>
-__device__ __forceinline__ void issue_w(uint8_t *dst, uint32_t wave, uint32_t t,
-                                        const uint8_t *const *wsrc)
+// s_waitcnt vmcnt(PER * ahead) for a wave-uniform ahead in 0..MAXA.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_vm_ahead(uint32_t ahead)
 {
-#pragma unroll
-    for (int u = 0; u < NW; ++u)
-        __builtin_amdgcn_global_load_lds(wsrc[u] + t * 128u,
-                                         (lds_void_t *)(dst + (wave * NW + u) * 1024u), 16, 0, 0);
+    if constexpr (MAXA <= 0) {
+        wait_vm<0>();
+    } else {
+        if (ahead >= (uint32_t)MAXA)
+            wait_vm<PER * MAXA>();
+        else
+            wait_vm_ahead<PER, MAXA - 1>(ahead);
+    }
 }
 
-template <int NT, int WST>
+template <int NT, int WST, int AST>
 __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr uint32_t kWBytes = NT * 128;
-    constexpr int NA = kABytes / 1024 / 4;   // A DMA instructions per wave per step
-    constexpr int NW = kWBytes / 1024 / 4;   // weight DMA instructions per wave per step
-    // LDS: two A buffers, then WST weight buffers.
+    constexpr int NA = kABytes / 1024 / 2;   // A DMA loads per odd wave per step
+    constexpr int NW = kWBytes / 1024 / 2;   // weight DMA loads per even wave per step
+    constexpr int NS = NA > NW ? NA : NW;
+    // LDS: AST A buffers, WST weight buffers, the split's scale row.
     uint8_t *const abuf = lds;
-    uint8_t *const wbuf = lds + 2 * kABytes;
+    uint8_t *const wbuf = lds + AST * kABytes;
+    float *const scl = reinterpret_cast<float *>(lds + AST * kABytes + WST * kWBytes);
     constexpr int NBW = NT / 32;             // 16-column blocks per wave
-    static_assert(NW >= 1 && NBW >= 1, "tile too small");
+    static_assert(NW >= 1 && NBW >= 1 && AST >= 2 && WST >= 2, "tile too small");
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave & 1u, wn = wave >> 1;
+    const bool wrole = (wave & 1u) == 0;     // even: weight ring, odd: A ring
+    const uint32_t grp = wave >> 1;          // which half of its ring's loads
     const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
     const uint32_t split = lid % g.splits;
     const uint32_t tile = lid / g.splits;
@@ -100,16 +115,13 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     const uint32_t ksteps = g.k / 128u;
     const uint32_t s0 = split * g.steps_per_split;
     const uint32_t s1 = min(ksteps, s0 + g.steps_per_split);
-    // Logical step t of the split is physical step s0 + (t - s0 + rot) mod
-    // span: tiles start their K walks at different offsets, which spreads
-    // concurrent weight reads over the HBM channels for power-of-two K.
-    const uint32_t span = s1 - s0;
-    const uint32_t rot = span ? (tile * kRotStride) % span : 0u;
-    auto phys = [&](uint32_t t) {
-        uint32_t x = t - s0 + rot;
-        x = x >= span ? x - span : x;
-        return s0 + x;
-    };
+    // All tiles of a split walk its K steps in the same order, so the tiles
+    // sharing an L2 read each A step at about the same time and only the
+    // first misses.  (Rotating the walk per tile, as the small-m kernels do
+    // to spread weight reads over HBM channels, measured slower here: with
+    // 512 KiB of weight streaming through each L2 per step, A steps read far
+    // apart are evicted in between.)
+    auto phys = [](uint32_t t) { return t; };
 
     // ---- DMA sources.  In LDS, A is two planes (K-step bytes 0..127 and
     // 128..255 of each row), each 128 rows x 128 bytes; the weight is NT rows
@@ -119,24 +131,25 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     // LDS bank conflicts on gfx950, which 256-byte rows are not.  A DMA
     // instruction fills 1 KiB of LDS = 8 rows of one plane; lane s writes
     // slot s % 8 of row s / 8, so it reads the chunk that slot holds.
-    const uint8_t *asrc[NA];
+    const uint8_t *src[NS];
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
-        const uint32_t i = wave * NA + u;          // 0..31: plane i / 16, rows 8(i % 16)..+7
-        const uint32_t plane = i >> 4;
-        const uint32_t r = 8u * (i & 15u) + (lane >> 3);
-        const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
-        const uint32_t row = min(m0 + r, g.m - 1u);
-        asrc[u] = g.a + (size_t)row * g.a_stride * 2u + c * 16u;
-    }
-    const uint8_t *wsrc[NW];
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-        const uint32_t i = wave * NW + u;          // rows 8i..8i+7
-        const uint32_t r = 8u * i + (lane >> 3);
-        const uint32_t c = (lane & 7u) ^ wswz(r & 15u);
-        const uint32_t row = min(n0 + r, g.n - 1u);
-        wsrc[u] = g.w + (size_t)row * g.k + c * 16u;
+    for (int u = 0; u < NS; ++u) {
+        if (!wrole && u < NA) {
+            const uint32_t i = grp * NA + u;          // 0..31: plane i / 16, rows 8(i % 16)..+7
+            const uint32_t plane = i >> 4;
+            const uint32_t r = 8u * (i & 15u) + (lane >> 3);
+            const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
+            const uint32_t row = min(m0 + r, g.m - 1u);
+            src[u] = g.a + (size_t)row * g.a_stride * 2u + c * 16u;
+        } else if (wrole && u < NW) {
+            const uint32_t i = grp * NW + u;          // rows 8i..8i+7
+            const uint32_t r = 8u * i + (lane >> 3);
+            const uint32_t c = (lane & 7u) ^ wswz(r & 15u);
+            const uint32_t row = min(n0 + r, g.n - 1u);
+            src[u] = g.w + (size_t)row * g.k + c * 16u;
+        } else {
+            src[u] = g.w;
+        }
     }
     // ---- MFMA operand reads: row rr = lane % 16 of a 16-row block, lane
     // group gq = lane / 16 covers physical k 32gq..32gq+31 of the step (MFMA
@@ -156,14 +169,6 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
         for (int h = 0; h < 2; ++h)
             woff[j][h] = ((NT / 2) * wn + 16u * j + rr) * 128u +
                          (((2u * gq + h) ^ wswz(rr)) * 16u);
-    // Scales of the tile's 128-row block for this split's steps (at most 64,
-    // which the planner guarantees), one per lane: lane l holds step s0 + l.
-    // They are loaded and waited for before any DMA is issued, so the loop
-    // has no vector loads of its own; each step reads its scale with readlane.
-    const float *srow = g.scale + (size_t)(min(n0, g.n - 1u) / 128u) * ksteps;
-    const float svec = (s0 + lane < s1) ? srow[s0 + lane] : 0.f;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
-
     f32x4_t acc[NBW][4];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
@@ -171,38 +176,49 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
         for (int b = 0; b < 4; ++b)
             acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Issue order, also in the prologue: iteration i issues A(i + 1), then
-    // W(i + WST - 1).  The weight (from HBM) runs WST - 1 steps ahead, A (from
-    // L2) one step ahead.
+    // Prologue.  Wave 1 first moves the scales of the tile's 128-row block
+    // for this split's steps (at most 64, which the planner guarantees) into
+    // LDS, lane l taking step s0 + l; its first wait covers them.
+    if (wrole) {
 #pragma unroll
-    for (int st = 0; st < WST - 2; ++st)
-        if (s0 + st < s1)
-            issue_w<NW>(wbuf + st * kWBytes, wave, phys(s0 + st), wsrc);
-    if (s0 < s1)
-        issue_a<NA>(abuf, wave, phys(s0), asrc);
-    if (s0 + WST - 2 < s1)
-        issue_w<NW>(wbuf + (WST - 2) * kWBytes, wave, phys(s0 + WST - 2), wsrc);
+        for (int st = 0; st < WST - 1; ++st)
+            if (s0 + st < s1)
+                issue_ring<NW, 128u>(wbuf + st * kWBytes, grp, phys(s0 + st), src);
+    } else {
+        if (wave == 1 && s0 < s1) {
+            const float *srow = g.scale + (size_t)(min(n0, g.n - 1u) / 128u) * ksteps;
+            __builtin_amdgcn_global_load_lds(srow + min(s0 + lane, s1 - 1u),
+                                             (lds_void_t *)scl, 4, 0, 0);
+        }
+#pragma unroll
+        for (int st = 0; st < AST - 1; ++st)
+            if (s0 + st < s1)
+                issue_ring<NA, 256u>(abuf + st * kABytes, grp, phys(s0 + st), src);
+    }
 
     for (uint32_t t = s0; t < s1; ++t) {
         const uint32_t idx = t - s0;
-        // A(t) was issued one iteration ago, followed only by W(t + WST - 2)
-        // (when that step exists); W(t) was issued before A(t).  So this
-        // wave's DMA for step t is complete once at most that weight group is
-        // outstanding.
-        if (t + WST - 2 < s1)
-            wait_vm<NW>();
+        // This wave's ring holds min(RING - 2, s1 - 1 - t) steps issued after
+        // step t; wait until only those are outstanding.
+        if (wrole)
+            wait_vm_ahead<NW, WST - 2>(min((uint32_t)(WST - 2), s1 - 1u - t));
         else
-            wait_vm<0>();
+            wait_vm_ahead<NA, AST - 2>(min((uint32_t)(AST - 2), s1 - 1u - t));
         barrier_lds();
-        if (t + 1 < s1)
-            issue_a<NA>(abuf + ((idx + 1) & 1u) * kABytes, wave, phys(t + 1), asrc);
-        if (t + WST - 1 < s1)
-            issue_w<NW>(wbuf + ((idx + WST - 1) % WST) * kWBytes, wave, phys(t + WST - 1), wsrc);
+        // Every wave is past step t - 1: refill the buffers it used.
+        if (wrole) {
+            if (t + WST - 1 < s1)
+                issue_ring<NW, 128u>(wbuf + ((idx + WST - 1) % WST) * kWBytes, grp,
+                                     phys(t + WST - 1), src);
+        } else {
+            if (t + AST - 1 < s1)
+                issue_ring<NA, 256u>(abuf + ((idx + AST - 1) % AST) * kABytes, grp,
+                                     phys(t + AST - 1), src);
+        }
 
-        const uint8_t *sa = abuf + (idx & 1u) * kABytes;
+        const uint8_t *sa = abuf + (idx % AST) * kABytes;
         const uint8_t *sw = wbuf + (idx % WST) * kWBytes;
-        const float s = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, svec), (int)(phys(t) - s0)));
+        const float s = scl[phys(t) - s0];
         u32x4_t wraw[NBW][2];
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
@@ -279,10 +295,10 @@ __global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uin
     store_c4(g, s, row, col);
 }
 
-template <int NT, int WST>
+template <int NT, int WST, int AST>
 hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    auto kern = w8a16_tile_kernel<NT, WST>;
+    auto kern = w8a16_tile_kernel<NT, WST, AST>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -309,13 +325,17 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
 
 hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    switch (p.n_blocks * 10 + p.depth) {
-    case 44: return launch_tile_t<64, 4>(g, p, stream);
-    case 46: return launch_tile_t<64, 6>(g, p, stream);
-    case 48: return launch_tile_t<64, 8>(g, p, stream);
-    case 83: return launch_tile_t<128, 3>(g, p, stream);
-    case 84: return launch_tile_t<128, 4>(g, p, stream);
-    case 85: return launch_tile_t<128, 5>(g, p, stream);
+    const int ast = (p.flags & W8A16_FLAG_A3) ? 3 : 2;
+    switch (p.n_blocks * 100 + p.depth * 10 + ast) {
+    case 442: return launch_tile_t<64, 4, 2>(g, p, stream);
+    case 462: return launch_tile_t<64, 6, 2>(g, p, stream);
+    case 482: return launch_tile_t<64, 8, 2>(g, p, stream);
+    case 443: return launch_tile_t<64, 4, 3>(g, p, stream);
+    case 463: return launch_tile_t<64, 6, 3>(g, p, stream);
+    case 832: return launch_tile_t<128, 3, 2>(g, p, stream);
+    case 842: return launch_tile_t<128, 4, 2>(g, p, stream);
+    case 852: return launch_tile_t<128, 5, 2>(g, p, stream);
+    case 833: return launch_tile_t<128, 3, 3>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -111,7 +111,9 @@ enum {
     W8A16_FLAG_DIRECT = 1u,
     /* Ring kernel, m <= 8 with m_blocks == 1: stage 8 A rows instead of 16
      * (derived by w8a16_plan_finalize from m; callers need not set it). */
-    W8A16_FLAG_A8 = 2u
+    W8A16_FLAG_A8 = 2u,
+    /* Tile kernel: three A buffers (A two steps ahead) instead of two. */
+    W8A16_FLAG_A3 = 4u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

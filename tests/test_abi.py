@@ -170,7 +170,10 @@ def test_large_m_plans_tile_kernel():
     assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (8, 8, 4, 16)
     assert p.grid == 256 and p.counter_count == 0
     assert p.workspace_bytes == 4 * 128 * 8192 * 4
-    assert p.lds_bytes == 2 * 128 * 256 + p.depth * 128 * 128 <= 160 * 1024 - 256
+    assert p.lds_bytes == 2 * 128 * 256 + p.depth * 128 * 128 + 256 <= 160 * 1024 - 256
+    p3 = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 8, 4, depth=3, flags=w8.FLAG_A3,
+                      waves=4)
+    assert p3.lds_bytes == 3 * 128 * 256 + 3 * 128 * 128 + 256
     # a split may not exceed 64 K steps (one scale per lane)
     p = w8.plan(100, 256, 128 * 200)
     assert p.steps_per_split <= 64
@@ -183,6 +186,12 @@ def test_large_m_plans_tile_kernel():
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 4, 1, depth=5, waves=4)
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 4, 8, 1, depth=3, waves=4)
+    with pytest.raises(w8.W8A16Error):      # three A buffers leave room for 3 weight buffers
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=4, flags=w8.FLAG_A3,
+                     waves=4)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=3, flags=w8.FLAG_A8,
+                     waves=4)
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():

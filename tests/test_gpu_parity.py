@@ -199,16 +199,19 @@ def test_ring_kernel_strides_and_short_k(w8):
         assert ran >= 2
 
 
-TILE_VARIANTS = [(8, 3), (8, 4), (8, 5), (4, 4), (4, 6), (4, 8)]
+TILE_VARIANTS = [(8, 3, 0), (8, 4, 0), (8, 5, 0), (8, 3, 4), (4, 4, 0), (4, 6, 0), (4, 8, 0),
+                 (4, 4, 4), (4, 6, 4)]
 
 
-@pytest.mark.parametrize("nb,depth", TILE_VARIANTS)
+@pytest.mark.parametrize("nb,depth,flags", TILE_VARIANTS)
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("m", [65, 128, 200])
-def test_exact_data_every_tile_variant(w8, nb, depth, splits, m):
-    n, k = 16 * nb * 3 + 7, 128 * 7
-    p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits)
-    plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, nb, splits, depth=depth, flags=0, waves=4)
+def test_exact_data_every_tile_variant(w8, nb, depth, flags, splits, m):
+    """K long enough for both rings to wrap, in every split."""
+    n, k = 16 * nb * 3 + 7, 128 * 23
+    p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits + flags)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, nb, splits, depth=depth, flags=flags,
+                        waves=4)
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
 
@@ -216,9 +219,9 @@ def test_exact_data_every_tile_variant(w8, nb, depth, splits, m):
 def test_tile_kernel_long_k_and_strides(w8):
     p = datagen.make_problem(130, 300, 128 * 40, seed=21, a_row_stride=128 * 40 + 24,
                              c_row_stride=311, c_extra_rows=2)
-    for nb, depth, splits in [(8, 5, 1), (8, 3, 4), (4, 6, 5)]:
+    for nb, depth, splits, flags in [(8, 5, 1, 0), (8, 3, 4, 4), (4, 6, 5, 0), (4, 4, 2, 4)]:
         plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_TILE, 8, nb, splits, depth=depth,
-                            flags=0, waves=4)
+                            flags=flags, waves=4)
         g = run_gpu(w8, p, plan)
         check_full(p, g)
         assert np.array_equal(g, run_gpu(w8, p, plan))
