@@ -160,9 +160,11 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if ((p->flags & ~(uint32_t)W8A16_FLAG_A3) != 0 || (p->waves != 0 && p->waves != 4)) {
+        if ((p->flags & ~(uint32_t)W8A16_FLAG_A3) != 0 ||
+            (p->waves != 0 && p->waves != 4 && p->waves != 6 && p->waves != 8 &&
+             p->waves != 10)) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel takes only the A3 flag and 4 waves "
+                     "w8a16_plan: tile kernel takes only the A3 flag and 4, 6, 8 or 10 waves "
                      "(flags=0x%x, waves=%u)", p->flags, p->waves);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
@@ -178,9 +180,16 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "A buffers", p->depth, p->n_blocks, ast);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        p->waves = 4;
+        if (p->waves == 0)
+            p->waves = 4;
+        if (!tile_variant_ok(p->n_blocks, ast, p->waves)) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: tile kernel has no %u-wave variant for n_blocks=%u with %u "
+                     "A buffers", p->waves, p->n_blocks, ast);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
         p->stage_steps = 0;
-        p->block = kTileThreads;
+        p->block = p->waves * 64;
         p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth, ast);
     } else {
         snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
@@ -248,7 +257,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.m_blocks = 8;
         p.n_blocks = 8;
         p.depth = 3;   // measured best of 3..5 weight buffers at 128 x 8192 x 8192
-        p.waves = 4;
+        p.waves = 8;   // two groups per K step: two waves per SIMD
         p.flags = 0;
         const uint32_t tiles = div_up(m, kTileRows) * div_up(n, 128);
         p.splits = 1;

@@ -16,7 +16,6 @@ constexpr uint32_t kDefaultCUs = 256;            // MI355X
 // Dynamic LDS a plan may use: the 160 KiB of a gfx950 CU less room for the
 // kernels' small static __shared__ variables.
 constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 256;
-constexpr uint32_t kTileThreads = 256;           // tile kernel: 4 waves
 constexpr uint32_t kTileRows = 128;              // tile kernel: rows of C per tile
 constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per split (one per lane)
 
@@ -27,6 +26,23 @@ constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per spl
 constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t w_stages, uint32_t a_stages)
 {
     return a_stages * kTileRows * 256 + w_stages * 16 * n_blocks * 128 + 256;
+}
+
+// Tile kernel wave counts: 4 (one wave per SIMD), 8 (two groups splitting
+// every K step), and 6 or 10 (those plus two producer waves that only issue
+// the LDS DMA).  Variants that would spill registers are not built: with
+// producers, a SIMD holds three waves of the 8-wave layout (10 waves), which
+// fits only the 64-column tile, and the 6-wave 128-column tile fits only two
+// A buffers.
+constexpr bool tile_variant_ok(uint32_t n_blocks, uint32_t a_stages, uint32_t waves)
+{
+    if (waves == 4 || waves == 8)
+        return true;
+    if (waves == 6)
+        return n_blocks == 4 || a_stages == 2;
+    if (waves == 10)
+        return n_blocks == 4;
+    return false;
 }
 
 // Ring kernel geometry, shared by the planner and the kernel dispatch.  A

@@ -47,6 +47,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace w8a16 {
 
@@ -71,6 +72,40 @@ __device__ __forceinline__ void issue_ring(uint8_t *dst, uint32_t grp, uint32_t 
                                          (lds_void_t *)(dst + (grp * N + u) * 1024u), 16, 0, 0);
 }
 
+// Producer-wave forms: the whole ring's loads of one step, each address
+// computed at issue (a producer has no math to overlap, and keeping 32
+// pointers live would cost the compute waves registers).  Same LDS image as
+// the shared forms: A load i fills plane i / 16, rows 8(i % 16)..+7; weight
+// load i fills rows 8i..8i+7; lane s writes slot s % 8 of row s / 8.
+template <int N>
+__device__ __forceinline__ void issue_a_all(uint8_t *dst, uint32_t t, const GemmArgs &g,
+                                            uint32_t m0, uint32_t lane)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t plane = (uint32_t)i >> 4;
+        const uint32_t r = 8u * ((uint32_t)i & 15u) + (lane >> 3);
+        const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
+        const uint32_t row = min(m0 + r, g.m - 1u);
+        __builtin_amdgcn_global_load_lds(g.a + (size_t)row * g.a_stride * 2u + c * 16u + t * 256u,
+                                         (lds_void_t *)(dst + i * 1024u), 16, 0, 0);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void issue_w_all(uint8_t *dst, uint32_t t, const GemmArgs &g,
+                                            uint32_t n0, uint32_t lane)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t r = 8u * (uint32_t)i + (lane >> 3);
+        const uint32_t c = (lane & 7u) ^ wswz(r & 15u);
+        const uint32_t row = min(n0 + r, g.n - 1u);
+        __builtin_amdgcn_global_load_lds(g.w + (size_t)row * g.k + c * 16u + t * 128u,
+                                         (lds_void_t *)(dst + i * 1024u), 16, 0, 0);
+    }
+}
+
 // s_waitcnt vmcnt(PER * ahead) for a wave-uniform ahead in 0..MAXA.
 template <int PER, int MAXA>
 __device__ __forceinline__ void wait_vm_ahead(uint32_t ahead)
@@ -85,14 +120,20 @@ __device__ __forceinline__ void wait_vm_ahead(uint32_t ahead)
     }
 }
 
-template <int NT, int WST, int AST>
-__global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
+template <int NT, int WST, int AST, int KH, bool PROD>
+__global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr uint32_t kWBytes = NT * 128;
-    constexpr int NA = kABytes / 1024 / 2;   // A DMA loads per odd wave per step
-    constexpr int NW = kWBytes / 1024 / 2;   // weight DMA loads per even wave per step
-    constexpr int NS = NA > NW ? NA : NW;
+    constexpr uint32_t CW = 4 * KH;          // compute waves
+    // Loads per issuing wave per step: with PROD one producer wave issues a
+    // whole ring, else the even compute waves share the weight ring and the
+    // odd ones the A ring.
+    constexpr int NA = kABytes / 1024 / (PROD ? 1 : 2 * KH);
+    constexpr int NW = kWBytes / 1024 / (PROD ? 1 : 2 * KH);
+    constexpr int QW = 4 / KH;               // MFMA k-quarters of a step per wave
+    constexpr int HW = 2 / KH;               // 16-byte weight chunks per row per wave
+    constexpr int NS = PROD ? 1 : (NA > NW ? NA : NW);
     // LDS: AST A buffers, WST weight buffers, the split's scale row.
     uint8_t *const abuf = lds;
     uint8_t *const wbuf = lds + AST * kABytes;
@@ -102,9 +143,13 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t wm = wave & 1u, wn = wave >> 1;
-    const bool wrole = (wave & 1u) == 0;     // even: weight ring, odd: A ring
-    const uint32_t grp = wave >> 1;          // which half of its ring's loads
+    const uint32_t wm = wave & 1u, wn = (wave >> 1) & 1u;
+    const uint32_t kh = (wave >> 2) & 1u;    // which k-quarters of each step (KH == 2)
+    const bool computes = !PROD || wave < CW;
+    const bool issues = !PROD || wave >= CW;
+    const bool wrole = PROD ? wave == CW : (wave & 1u) == 0;   // weight ring, else A ring
+    const uint32_t grp = PROD ? 0u : wave >> 1;                // share of its ring's loads
+    const bool scale_wave = wave == (PROD ? CW + 1 : 1u);
     const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
     const uint32_t split = lid % g.splits;
     const uint32_t tile = lid / g.splits;
@@ -134,7 +179,9 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     const uint8_t *src[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        if (!wrole && u < NA) {
+        if (PROD || !issues) {
+            src[u] = g.w;
+        } else if (!wrole && u < NA) {
             const uint32_t i = grp * NA + u;          // 0..31: plane i / 16, rows 8(i % 16)..+7
             const uint32_t plane = i >> 4;
             const uint32_t r = 8u * (i & 15u) + (lane >> 3);
@@ -155,20 +202,27 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     // group gq = lane / 16 covers physical k 32gq..32gq+31 of the step (MFMA
     // q takes k 32gq+8q..+7 from both operands).
     const uint32_t rr = lane & 15u, gq = lane >> 4;
-    uint32_t aoff[4][4];
+    // With KH == 2 the two groups of four waves take k-quarters 0-1 and 2-3
+    // of every step over the same staged buffers, so each SIMD runs two
+    // waves: one wave's LDS and barrier waits overlap the other's MFMAs.
+    uint32_t aoff[4][QW];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            aoff[b][q] = ((4u * gq + q) >> 3) * (kTileM * 128u) + (64u * wm + 16u * b + rr) * 128u +
-                         ((((4u * gq + q) & 7u) ^ wswz(rr)) * 16u);
-    uint32_t woff[NBW][2];
+        for (int qq = 0; qq < QW; ++qq) {
+            const uint32_t q = kh * QW + qq;
+            aoff[b][qq] = ((4u * gq + q) >> 3) * (kTileM * 128u) + (64u * wm + 16u * b + rr) * 128u +
+                          ((((4u * gq + q) & 7u) ^ wswz(rr)) * 16u);
+        }
+    uint32_t woff[NBW][HW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            woff[j][h] = ((NT / 2) * wn + 16u * j + rr) * 128u +
-                         (((2u * gq + h) ^ wswz(rr)) * 16u);
+        for (int hh = 0; hh < HW; ++hh) {
+            const uint32_t h = kh * HW + hh;
+            woff[j][hh] = ((NT / 2) * wn + 16u * j + rr) * 128u +
+                          (((2u * gq + h) ^ wswz(rr)) * 16u);
+        }
     f32x4_t acc[NBW][4];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
@@ -179,68 +233,91 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
     // Prologue.  Wave 1 first moves the scales of the tile's 128-row block
     // for this split's steps (at most 64, which the planner guarantees) into
     // LDS, lane l taking step s0 + l; its first wait covers them.
-    if (wrole) {
+    if (!issues) {
+    } else if (wrole) {
 #pragma unroll
         for (int st = 0; st < WST - 1; ++st)
-            if (s0 + st < s1)
-                issue_ring<NW, 128u>(wbuf + st * kWBytes, grp, phys(s0 + st), src);
+            if (s0 + st < s1) {
+                if constexpr (PROD)
+                    issue_w_all<NW>(wbuf + st * kWBytes, phys(s0 + st), g, n0, lane);
+                else
+                    issue_ring<NW, 128u>(wbuf + st * kWBytes, grp, phys(s0 + st), src);
+            }
     } else {
-        if (wave == 1 && s0 < s1) {
+        if (scale_wave && s0 < s1) {
             const float *srow = g.scale + (size_t)(min(n0, g.n - 1u) / 128u) * ksteps;
             __builtin_amdgcn_global_load_lds(srow + min(s0 + lane, s1 - 1u),
                                              (lds_void_t *)scl, 4, 0, 0);
         }
 #pragma unroll
         for (int st = 0; st < AST - 1; ++st)
-            if (s0 + st < s1)
-                issue_ring<NA, 256u>(abuf + st * kABytes, grp, phys(s0 + st), src);
+            if (s0 + st < s1) {
+                if constexpr (PROD)
+                    issue_a_all<NA>(abuf + st * kABytes, phys(s0 + st), g, m0, lane);
+                else
+                    issue_ring<NA, 256u>(abuf + st * kABytes, grp, phys(s0 + st), src);
+            }
     }
 
     for (uint32_t t = s0; t < s1; ++t) {
         const uint32_t idx = t - s0;
-        // This wave's ring holds min(RING - 2, s1 - 1 - t) steps issued after
-        // step t; wait until only those are outstanding.
-        if (wrole)
-            wait_vm_ahead<NW, WST - 2>(min((uint32_t)(WST - 2), s1 - 1u - t));
-        else
-            wait_vm_ahead<NA, AST - 2>(min((uint32_t)(AST - 2), s1 - 1u - t));
+        // An issuing wave's ring holds min(RING - 2, s1 - 1 - t) steps issued
+        // after step t; wait until only those are outstanding.
+        if (issues) {
+            if (wrole)
+                wait_vm_ahead<NW, WST - 2>(min((uint32_t)(WST - 2), s1 - 1u - t));
+            else
+                wait_vm_ahead<NA, AST - 2>(min((uint32_t)(AST - 2), s1 - 1u - t));
+        }
         barrier_lds();
         // Every wave is past step t - 1: refill the buffers it used.
-        if (wrole) {
-            if (t + WST - 1 < s1)
-                issue_ring<NW, 128u>(wbuf + ((idx + WST - 1) % WST) * kWBytes, grp,
-                                     phys(t + WST - 1), src);
-        } else {
-            if (t + AST - 1 < s1)
-                issue_ring<NA, 256u>(abuf + ((idx + AST - 1) % AST) * kABytes, grp,
-                                     phys(t + AST - 1), src);
+        if (issues) {
+            if (wrole) {
+                if (t + WST - 1 < s1) {
+                    uint8_t *dst = wbuf + ((idx + WST - 1) % WST) * kWBytes;
+                    if constexpr (PROD)
+                        issue_w_all<NW>(dst, phys(t + WST - 1), g, n0, lane);
+                    else
+                        issue_ring<NW, 128u>(dst, grp, phys(t + WST - 1), src);
+                }
+            } else {
+                if (t + AST - 1 < s1) {
+                    uint8_t *dst = abuf + ((idx + AST - 1) % AST) * kABytes;
+                    if constexpr (PROD)
+                        issue_a_all<NA>(dst, phys(t + AST - 1), g, m0, lane);
+                    else
+                        issue_ring<NA, 256u>(dst, grp, phys(t + AST - 1), src);
+                }
+            }
         }
+        if (!computes)
+            continue;
 
         const uint8_t *sa = abuf + (idx % AST) * kABytes;
         const uint8_t *sw = wbuf + (idx % WST) * kWBytes;
         const float s = scl[phys(t) - s0];
-        u32x4_t wraw[NBW][2];
+        u32x4_t wraw[NBW][HW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                wraw[j][h] = *reinterpret_cast<const u32x4_t *>(sw + woff[j][h]);
+            for (int hh = 0; hh < HW; ++hh)
+                wraw[j][hh] = *reinterpret_cast<const u32x4_t *>(sw + woff[j][hh]);
         f32x4_t p[NBW][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int qq = 0; qq < QW; ++qq) {
             bf16x8_t af[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                af[b] = *reinterpret_cast<const bf16x8_t *>(sa + aoff[b][q]);
+                af[b] = *reinterpret_cast<const bf16x8_t *>(sa + aoff[b][qq]);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
                 bf16x8_t lo, hi;
-                dequant16(wraw[j][q >> 1], lo, hi);
-                const bf16x8_t wb = (q & 1) ? hi : lo;
+                dequant16(wraw[j][qq >> 1], lo, hi);
+                const bf16x8_t wb = (qq & 1) ? hi : lo;
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     p[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        wb, af[b], q == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : p[j][b], 0, 0, 0);
+                        wb, af[b], qq == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : p[j][b], 0, 0, 0);
             }
         }
 #pragma unroll
@@ -254,6 +331,31 @@ __global__ __launch_bounds__(256) void w8a16_tile_kernel(GemmArgs g)
             }
     }
 
+    // ---- with KH == 2 the second group hands its sums to the first through
+    // LDS (every wave has waited for all its loads: the last step waits for
+    // none outstanding), and the first adds them: acc = group 0 + group 1.
+    if constexpr (KH == 2) {
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);   // [4 waves][NBW][4][64]
+        barrier_lds();
+        if (computes && kh == 1) {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    red[(((wave & 3u) * NBW + j) * 4 + b) * 64 + lane] = acc[j][b];
+        }
+        barrier_lds();
+        if (!computes || kh == 1)
+            return;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[j][b] += red[((wave * NBW + j) * 4 + b) * 64 + lane];
+    }
+
+    if (!computes)
+        return;
     // ---- epilogue: lane holds C[row][col..col+3] of each (j, b) tile.
     const uint32_t row_off = 64u * wm + rr;
     const uint32_t col_off = (NT / 2) * wn + 4u * gq;
@@ -295,10 +397,14 @@ __global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uin
     store_c4(g, s, row, col);
 }
 
-template <int NT, int WST, int AST>
+template <int NT, int WST, int AST, int KH, bool PROD>
 hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    auto kern = w8a16_tile_kernel<NT, WST, AST>;
+    if constexpr (!tile_variant_ok(NT / 16, AST, 4 * KH + (PROD ? 2 : 0))) {
+        (void)g, (void)p, (void)stream;
+        return hipErrorInvalidValue;
+    } else {
+    auto kern = w8a16_tile_kernel<NT, WST, AST, KH, PROD>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -319,6 +425,19 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
     hipLaunchKernelGGL(w8a16_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, g, ws_cols,
                        ws_rows);
     return hipGetLastError();
+    }
+}
+
+template <int NT, int WST, int AST>
+hipError_t launch_tile_k(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    switch (p.waves) {
+    case 4: return launch_tile_t<NT, WST, AST, 1, false>(g, p, stream);
+    case 6: return launch_tile_t<NT, WST, AST, 1, true>(g, p, stream);
+    case 8: return launch_tile_t<NT, WST, AST, 2, false>(g, p, stream);
+    case 10: return launch_tile_t<NT, WST, AST, 2, true>(g, p, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -327,15 +446,15 @@ hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t str
 {
     const int ast = (p.flags & W8A16_FLAG_A3) ? 3 : 2;
     switch (p.n_blocks * 100 + p.depth * 10 + ast) {
-    case 442: return launch_tile_t<64, 4, 2>(g, p, stream);
-    case 462: return launch_tile_t<64, 6, 2>(g, p, stream);
-    case 482: return launch_tile_t<64, 8, 2>(g, p, stream);
-    case 443: return launch_tile_t<64, 4, 3>(g, p, stream);
-    case 463: return launch_tile_t<64, 6, 3>(g, p, stream);
-    case 832: return launch_tile_t<128, 3, 2>(g, p, stream);
-    case 842: return launch_tile_t<128, 4, 2>(g, p, stream);
-    case 852: return launch_tile_t<128, 5, 2>(g, p, stream);
-    case 833: return launch_tile_t<128, 3, 3>(g, p, stream);
+    case 442: return launch_tile_k<64, 4, 2>(g, p, stream);
+    case 462: return launch_tile_k<64, 6, 2>(g, p, stream);
+    case 482: return launch_tile_k<64, 8, 2>(g, p, stream);
+    case 443: return launch_tile_k<64, 4, 3>(g, p, stream);
+    case 463: return launch_tile_k<64, 6, 3>(g, p, stream);
+    case 832: return launch_tile_k<128, 3, 2>(g, p, stream);
+    case 842: return launch_tile_k<128, 4, 2>(g, p, stream);
+    case 852: return launch_tile_k<128, 5, 2>(g, p, stream);
+    case 833: return launch_tile_k<128, 3, 3>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
