@@ -17,6 +17,7 @@ same calls issued one by one (eager) are timed too and reported beside it.
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only-main]
     python bench.py --traffic-run          (workload for rocprofv3 --pmc runs)
+    python bench.py --m-sweep N K          (default plan for m = 1..256, one line each)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 
@@ -116,16 +117,22 @@ def time_workload(torch, w8, prob, steps: int, warmup: int, cold: bool = True,
     return arena, graph_ms, eager_ms, replicas
 
 
-def check_arena_output(arena, oracle, datagen, torch):
-    """Sampled parity of the last replica written by the timed loop."""
-    p = arena.prob
+def check_arena_output(arena, calls: int):
+    """Sanity of every replica written by the `calls` timed and warm-up
+    calls (call i writes replica i mod replicas): all m x n outputs
+    finite BF16 and the pitch pad / extra rows still hold their sentinel.
+    (Numerical parity against the oracle is the GPU tests' job; the timed
+    legs of the benchmark do not run the oracle.)"""
     import numpy as np
-    c = arena.c[0].cpu().numpy().view(np.uint16).reshape(p.c.shape)
-    rows, cols = datagen.sample_indices(p.m, p.n, 512, seed=99)
-    oc, _, bound = oracle.gemm_at(p.a, p.w, p.scale, p.m, p.n, p.k, rows, cols,
-                                  a_row_stride=p.a_row_stride)
-    ok = oracle.within_tolerance(c[rows, cols], oc, bound)
-    return bool(ok.all())
+    p = arena.prob
+    ok = True
+    for i in range(min(arena.r, calls)):
+        c = arena.c[i].cpu().numpy().view(np.uint16).reshape(p.c.shape)
+        body = c[:p.m, :p.n]
+        ok &= bool(((body & 0x7F80) != 0x7F80).all())        # no Inf / NaN
+        ok &= bool((c[:p.m, p.n:] == p.c[:p.m, p.n:]).all())
+        ok &= bool((c[p.m:, :] == p.c[p.m:, :]).all())
+    return ok
 
 
 def cpu_baseline(oracle, datagen, prob, budget_s: float = 10.0):
@@ -293,7 +300,41 @@ def summarize_trace(trace_dir: str, wl_name: str, command: str):
     print(open(path).read())
 
 
+M_SWEEP = [1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64, 65, 80, 96, 112, 128, 160, 192, 256]
+
+
+def m_sweep(n: int, k: int, steps: int = 50):
+    """Default plan over the row counts of M_SWEEP at one (n, k): one JSON
+    line per m (cold weights, graph replay)."""
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    w8.library()
+    for m in M_SWEEP:
+        prob = datagen.make_problem(m, n, k, seed=7000 + m)
+        plan = w8.plan(m, n, k, torch.cuda.get_device_properties(0).multi_processor_count)
+        # one untimed pass first: the first timing of a fresh arena runs slow
+        ar, _, _, _ = time_workload(torch, w8, prob, 10, 3)
+        del ar
+        arena, ms, eager_ms, replicas = time_workload(torch, w8, prob, steps, 5)
+        ok = check_arena_output(arena, steps + 5)
+        del arena
+        torch.cuda.empty_cache()
+        nbytes = n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * k + 2 * m * n
+        print(json.dumps({"m": m, "n": n, "k": k, "us_per_call": round(ms * 1e3, 3),
+                          "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 2),
+                          "kernel": {w8.KERNEL_STREAM: "stream", w8.KERNEL_TILE: "tile",
+                                     w8.KERNEL_RING: "ring"}.get(plan.kernel, "?"),
+                          "plan": plan.as_dict(), "output_sane": ok}), flush=True)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--m-sweep":
+        n = int(sys.argv[2]) if len(sys.argv) > 2 else 8192
+        k = int(sys.argv[3]) if len(sys.argv) > 3 else 8192
+        m_sweep(n, k)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         wl_name = sys.argv[3] if len(sys.argv) > 3 else MAIN_WORKLOAD
         cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- python3 "
@@ -337,7 +378,6 @@ def main():
 
     import block_scaled_fp8_w8a16_amd as w8
     import datagen
-    import oracle
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -352,12 +392,12 @@ def main():
     log("timing %s plan=%s" % (wl.name, plan.as_dict()))
     arena, ms_call, eager_ms, replicas = time_workload(torch, w8, prob, args.steps,
                                                        args.warmup, cold=not args.warm)
-    parity_ok = check_arena_output(arena, oracle, datagen, torch)
+    sane = check_arena_output(arena, args.steps + args.warmup)
     del arena
     torch.cuda.empty_cache()
     alg_bytes = wl.algorithmic_bytes()
     gbs = alg_bytes / (ms_call * 1e-3) / 1e9
-    log("%s: %.3f us/call, %.1f GB/s (parity %s)" % (wl.name, ms_call * 1e3, gbs, parity_ok))
+    log("%s: %.3f us/call, %.1f GB/s (output sane %s)" % (wl.name, ms_call * 1e3, gbs, sane))
 
     traffic = load_traffic(wl.name, khash)
     result = {
@@ -383,7 +423,7 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(wl.flops() / (ms_call * 1e-3) / 1e12, 3),
         "plan": plan.as_dict(),
-        "parity_sampled_ok": parity_ok,
+        "output_sane": sane,
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 2),
@@ -408,31 +448,33 @@ def main():
                              "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2),
                              "tflops": result["tflops"],
                              "pct_mfma": round(100 * result["tflops"] / BF16_PEAK_TFLOPS, 2),
-                             "parity_sampled_ok": parity_ok, "plan": plan.as_dict()})
+                             "output_sane": sane, "plan": plan.as_dict()})
                 continue
             log("generating %s" % other.name)
             op = datagen.make_workload(other)
             oplan = w8.plan(other.m, other.n, other.k)
             steps = max(20, min(args.steps, 200))
-            ar, oms, oeager, orep = time_workload(torch, w8, op, steps, max(5, args.warmup // 2))
-            ok = check_arena_output(ar, oracle, datagen, torch)
+            owarm = max(5, args.warmup // 2)
+            ar, oms, oeager, orep = time_workload(torch, w8, op, steps, owarm)
+            ok = check_arena_output(ar, steps + owarm)
             del ar
             torch.cuda.empty_cache()
             ogbs = other.algorithmic_bytes() / (oms * 1e-3) / 1e9
             otf = other.flops() / (oms * 1e-3) / 1e12
-            log("%s: %.3f us/call, %.1f GB/s, %.1f TFLOP/s (parity %s)" %
+            log("%s: %.3f us/call, %.1f GB/s, %.1f TFLOP/s (output sane %s)" %
                 (other.name, oms * 1e3, ogbs, otf, ok))
             rows.append({"workload": other.name, "us_per_call": round(oms * 1e3, 3),
                          "us_per_call_eager": round(oeager * 1e3, 3),
                          "gbs": round(ogbs, 1), "pct_hbm": round(100 * ogbs / HBM_PEAK_GBS, 2),
                          "tflops": round(otf, 3),
                          "pct_mfma": round(100 * otf / BF16_PEAK_TFLOPS, 2),
-                         "parity_sampled_ok": ok, "plan": oplan.as_dict(),
+                         "output_sane": ok, "plan": oplan.as_dict(),
                          "arena_replicas": orep})
             del op
         result["all_workloads"] = rows
 
     if not args.no_cpu:
+        import oracle   # the CPU baseline leg is the only part that runs the oracle
         log("timing the CPU oracle on %s" % wl.name)
         dt, reps, threads = cpu_baseline(oracle, datagen, prob)
         result["cpu_baseline"] = {

@@ -194,6 +194,18 @@ def test_large_m_plans_tile_kernel():
                      waves=4)
 
 
+def test_large_m_prefers_64_column_tiles_over_short_splits():
+    # 128-column tiles would need 8 splits of 4 K steps; 64-column tiles
+    # fill the chip with 4 splits of 8 steps
+    p = w8.plan(96, 4096, 4096)
+    assert (p.kernel, p.n_blocks, p.splits, p.steps_per_split) == (w8.KERNEL_TILE, 4, 4, 8)
+    _covers(p, 96, 4096, 4096)
+    p = w8.plan(256, 4096, 4096)       # two row tiles: 4 splits of 8 steps already
+    assert (p.n_blocks, p.splits) == (8, 4)
+    p = w8.plan(128, 8192, 8192)
+    assert (p.n_blocks, p.splits, p.waves) == (8, 4, 8)
+
+
 def test_split_k_only_when_tiles_leave_cus_idle():
     p = w8.plan(1, 128, 65536)
     assert p.splits > 1 and p.grid <= 256

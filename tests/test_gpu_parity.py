@@ -278,10 +278,25 @@ def test_determinism_and_plans_agree_within_tolerance(w8):
 
 
 def test_m_sweep(w8):
-    for m in list(range(1, 41)) + [47, 63, 64, 65, 100]:
+    """Every row count the planner treats differently, 1..256."""
+    for m in list(range(1, 41)) + [47, 63, 64, 65, 100, 127, 128, 129, 160, 192, 255, 256]:
         p = datagen.make_problem(m, 272, 384, seed=300 + m, c_extra_rows=1)
         g = run_gpu(w8, p)
         check_full(p, g)
+
+
+@pytest.mark.parametrize("m,n,k", [(96, 4096, 4096), (192, 2048, 8192), (24, 8192, 8192),
+                                   (48, 4096, 4096)])
+def test_default_plans_at_size_sampled(w8, m, n, k):
+    """Default plans of the M sweep's larger shapes (64-column tiles, two row
+    tiles, ring with two row blocks, stream with four), sampled parity."""
+    p = datagen.make_problem(m, n, k, seed=m + n + k, c_extra_rows=1)
+    g = run_gpu(w8, p)
+    rows, cols = datagen.sample_indices(m, n, 300, seed=5)
+    oc, _, bound = oracle.gemm_at(p.a, p.w, p.scale, m, n, k, rows, cols,
+                                  a_row_stride=p.a_row_stride)
+    assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+    assert (g[m:, :] == p.c[m:, :]).all()
 
 
 def test_ragged_n_and_single_step(w8):
