@@ -37,7 +37,6 @@ KERNEL_RING = 3
 
 FLAG_DIRECT = 1
 FLAG_A8 = 2
-FLAG_A3 = 4
 
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
@@ -59,7 +58,8 @@ class Plan(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64),
                 ("counter_count", ctypes.c_uint32), ("cu_count", ctypes.c_uint32),
                 ("depth", ctypes.c_uint32), ("flags", ctypes.c_uint32),
-                ("waves", ctypes.c_uint32), ("stage_steps", ctypes.c_uint32)]
+                ("waves", ctypes.c_uint32), ("stage_steps", ctypes.c_uint32),
+                ("a_depth", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -124,12 +124,13 @@ def plan(m: int, n: int, k: int, cu_count: int = 0) -> Plan:
 
 def make_plan(m: int, n: int, k: int, kernel: int, m_blocks: int, n_blocks: int,
               splits: int, depth: int = 2, flags: int = 0, waves: int = 4,
-              cu_count: int = 0, stage_steps: int = 0) -> Plan:
+              cu_count: int = 0, stage_steps: int = 0, a_depth: int = 0) -> Plan:
     """A caller-chosen plan, checked and completed by the library."""
     p = Plan()
     p.kernel, p.m_blocks, p.n_blocks, p.splits, p.cu_count = \
         kernel, m_blocks, n_blocks, splits, cu_count
-    p.depth, p.flags, p.waves, p.stage_steps = depth, flags, waves, stage_steps
+    p.depth, p.flags, p.waves = depth, flags, waves
+    p.stage_steps, p.a_depth = stage_steps, a_depth
     _raise_if(library().w8a16_plan_finalize(m, n, k, ctypes.byref(p)))
     return p
 

@@ -6,6 +6,7 @@ in-tree next to this file so it travels with the source tree.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -16,8 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw8a16.so")
 
-SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_kernel.hip", "ring_kernel.hip"]
-HEADERS = ["plan.h", "kernels.h", "device_common.h"]
+SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_m64.hip", "tile_m128.hip",
+           "ring_kernel.hip"]
+HEADERS = ["plan.h", "kernels.h", "device_common.h", "tile_kernel.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,27 +31,33 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # FP32 accumulators with VALU FMAs; with the partials in AGPRs every fold
 # first copies them out (v_accvgpr_read), which measured as the single most
 # expensive part of its loop.  The VGPR form of the MFMA keeps them in VGPRs.
-EXTRA_FLAGS = {"tile_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"tile_m64.hip": _VGPR_FORM, "tile_m128.hip": _VGPR_FORM}
+
+
+def _compile_cmd(src: str, obj: str) -> list:
+    path = os.path.join(CSRC, src)
+    if src.endswith(".hip"):
+        return [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+                "-Wall", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS + \
+               EXTRA_FLAGS.get(src, []) + ["-c", path, "-o", obj]
+    return ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+            "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]
 
 
 def build(verbose: bool = False) -> str:
-    objs = []
+    """Compile every source (in parallel, at most 8 at a time) and link."""
     builddir = os.path.join(HERE, "_build")
     os.makedirs(builddir, exist_ok=True)
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(builddir, src + ".o")
-        if src.endswith(".hip"):
-            cmd = [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-                   "-Wall", "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS + \
-                  EXTRA_FLAGS.get(src, []) + ["-c", path, "-o", obj]
-        else:
-            cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
-                   "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]
-        if verbose:
+    objs = [os.path.join(builddir, src + ".o") for src in SOURCES]
+    cmds = [_compile_cmd(src, obj) for src, obj in zip(SOURCES, objs)]
+    if verbose:
+        for cmd in cmds:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        objs.append(obj)
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        for fut in [pool.submit(subprocess.run, cmd, check=True) for cmd in cmds]:
+            fut.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -148,7 +148,8 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
     else if (plan.kernel == W8A16_KERNEL_RING)
         e = launch_ring(g, plan, stream);
     else
-        e = launch_tile(g, plan, stream);
+        e = plan.m_blocks == 4 ? launch_tile_m64(g, plan, stream)
+                               : launch_tile_m128(g, plan, stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     set_last_error("");

@@ -24,7 +24,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
-hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_tile_m64(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_tile_m128(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_ring(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 
 }  // namespace w8a16

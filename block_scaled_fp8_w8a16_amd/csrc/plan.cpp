@@ -82,7 +82,7 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
 {
-    return mb == 8 && (nb == 4 || nb == 8);
+    return (mb == 4 || mb == 8) && (nb == 4 || nb == 8);
 }
 
 int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
@@ -117,6 +117,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         }
         p->block = p->waves * 64;
         p->stage_steps = 0;
+        p->a_depth = 0;
         const bool direct = (p->flags & W8A16_FLAG_DIRECT) != 0;
         uint32_t per_wave = p->n_blocks * kWBlockBytes + (direct ? 0u : p->m_blocks * kABlockBytes);
         uint32_t staging = p->waves * per_wave;
@@ -146,6 +147,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->block = p->waves * 64;
+        p->a_depth = 0;
         p->lds_bytes = ring_lds_bytes(p->m_blocks, p->n_blocks, p->stage_steps, p->depth, a8, ksteps);
         if (p->lds_bytes > kMaxLdsBytes) {
             snprintf(buf, sizeof buf,
@@ -160,37 +162,41 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if ((p->flags & ~(uint32_t)W8A16_FLAG_A3) != 0 ||
+        if (p->flags != 0 ||
             (p->waves != 0 && p->waves != 4 && p->waves != 6 && p->waves != 8 &&
              p->waves != 10)) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel takes only the A3 flag and 4, 6, 8 or 10 waves "
+                     "w8a16_plan: tile kernel takes no flags and 4, 6, 8 or 10 waves "
                      "(flags=0x%x, waves=%u)", p->flags, p->waves);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         // Built (weight buffers, A buffers) pairs; all fit in LDS.
-        const uint32_t ast = (p->flags & W8A16_FLAG_A3) ? 3u : 2u;
-        const bool depth_ok = p->n_blocks == 8
-                                  ? (ast == 2 ? (p->depth >= 3 && p->depth <= 5) : p->depth == 3)
-                                  : (ast == 2 ? (p->depth == 4 || p->depth == 6 || p->depth == 8)
-                                              : (p->depth == 4 || p->depth == 6));
-        if (!depth_ok) {
+        if (p->a_depth == 0)
+            p->a_depth = 2;
+        const uint32_t ast = p->a_depth;
+        if (!tile_depth_built(p->m_blocks, p->n_blocks, p->depth, ast)) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel has no depth=%u variant for n_blocks=%u with %u "
-                     "A buffers", p->depth, p->n_blocks, ast);
+                     "w8a16_plan: tile kernel has no depth=%u variant for m_blocks=%u, "
+                     "n_blocks=%u with %u A buffers", p->depth, p->m_blocks, p->n_blocks, ast);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         if (p->waves == 0)
             p->waves = 4;
-        if (!tile_variant_ok(p->n_blocks, ast, p->waves)) {
+        if (!tile_variant_ok(p->m_blocks, p->n_blocks, p->depth, ast, p->waves)) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel has no %u-wave variant for n_blocks=%u with %u "
-                     "A buffers", p->waves, p->n_blocks, ast);
+                     "w8a16_plan: tile kernel has no %u-wave variant for m_blocks=%u, "
+                     "n_blocks=%u with %u A buffers", p->waves, p->m_blocks, p->n_blocks, ast);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->stage_steps = 0;
         p->block = p->waves * 64;
-        p->lds_bytes = tile_lds_bytes(p->n_blocks, p->depth, ast);
+        p->lds_bytes = tile_lds_bytes(p->m_blocks, p->n_blocks, p->depth, ast);
+        if (p->lds_bytes > kMaxLdsBytes) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
+                     p->lds_bytes, kMaxLdsBytes);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
     } else {
         snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
         return fail(W8A16_ERR_BAD_PLAN, buf);
@@ -222,7 +228,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
     p->grid = (uint32_t)grid;
     if (p->splits > 1 && p->kernel == W8A16_KERNEL_TILE) {
         // whole FP32 tiles per split, added by a second kernel
-        p->workspace_bytes = (uint64_t)p->splits * p->m_tiles * kTileRows *
+        p->workspace_bytes = (uint64_t)p->splits * p->m_tiles * 16 * p->m_blocks *
                              p->n_tiles * 16 * p->n_blocks * 4;
         p->counter_count = 0;
     } else if (p->splits > 1) {
@@ -248,37 +254,43 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     const uint32_t ksteps = k / kKStep;
     const uint32_t nb16 = div_up(n, 16);
 
-    if (m > 64) {
-        // Large m: 128 x 128 tiles (128 x 64 when that needs fewer splits)
-        // that share each staged weight tile among all 128 rows.  K is
-        // split until the tiles fill the CUs: besides
-        // parallelism, a split cuts the A bytes every CU pulls from L2
-        // (all of A for a full-K tile), which is what bounds the tile.
+    // Above 32 rows a weight larger than 16 MiB goes through the tile
+    // kernel (one L2 pass of the weight per 64-row tile); smaller weights
+    // and up to 64 rows stream faster (measured on MI355X: 48 x 8192 x 8192
+    // 22 vs 32 us, 48 x 4096 x 4096 12.4 vs 12.2 us, 40 x 6144 x 2048 11.1
+    // vs 10.2 us).
+    const uint64_t wbytes = (uint64_t)n * k;
+    if (m > 64 || (m > 32 && wbytes > (16ull << 20))) {
+        // 64-row tiles up to 128 rows, 128-row tiles above (fewer weight
+        // passes).  The grid is one workgroup per CU: K is split until the
+        // tiles fill the CUs, with 128-column tiles when that leaves each
+        // split 16 or more K steps, else 64-column tiles (measured best at
+        // 48..128 rows over 4096- and 8192-square weights).  Ring sizes
+        // and waves are the measured best per tile shape.
         p.kernel = W8A16_KERNEL_TILE;
-        p.m_blocks = 8;
-        p.n_blocks = 8;
-        p.depth = 3;   // measured best of 3..5 weight buffers at 128 x 8192 x 8192
-        p.waves = 8;   // two groups per K step: two waves per SIMD
         p.flags = 0;
-        const uint32_t m_tiles = div_up(m, kTileRows);
-        auto splits_for = [&](uint32_t tiles) {
+        p.m_blocks = m <= 128 ? 4 : 8;
+        const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
+        auto splits_fill = [&](uint32_t tiles) {
             uint32_t sp = 1;
-            while (tiles * sp * 2 <= p.cu_count && ksteps >= 8 * sp)
+            while (tiles * sp * 2 <= p.cu_count && sp * 2 <= ksteps)
                 sp *= 2;
             return sp;
         };
-        p.splits = splits_for(m_tiles * div_up(n, 128));
-        // Splits that leave a workgroup under 8 K steps spend most of it
-        // filling and draining its rings; 64-column tiles then reach the
-        // CUs with half the splits (measured at 96 x 4096 x 4096: 18.4 vs
-        // 19.7 us).
-        if (ksteps / p.splits < 8) {
-            const uint32_t sp64 = splits_for(m_tiles * div_up(n, 64));
-            if (sp64 < p.splits) {
-                p.n_blocks = 4;
-                p.depth = 4;
-                p.splits = sp64;
-            }
+        p.n_blocks = 8;
+        p.splits = splits_fill(m_tiles * div_up(n, 128));
+        if (ksteps / p.splits < 16) {
+            p.n_blocks = 4;
+            p.splits = splits_fill(m_tiles * div_up(n, 64));
+        }
+        if (p.m_blocks == 4) {
+            p.depth = 4;
+            p.a_depth = p.n_blocks == 8 ? 4 : 6;
+            p.waves = p.n_blocks == 8 ? 10 : 8;
+        } else {
+            p.depth = p.n_blocks == 8 ? 3 : 4;
+            p.a_depth = 2;
+            p.waves = 8;
         }
         if (p.splits < div_up(ksteps, kTileMaxSteps))
             p.splits = div_up(ksteps, kTileMaxSteps);
@@ -321,7 +333,6 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         // A large weight (>= 48 MiB) with 8..32 rows streams faster through
         // the ring kernel's row-contiguous LDS-DMA stages (measured 3-9 %);
         // below that, or with fewer rows, its slower start does not pay off.
-        const uint64_t wbytes = (uint64_t)n * k;
         const uint32_t rmb = m <= 16 ? 1 : 2;
         if (m >= 8 && m <= 32 && wbytes >= (48ull << 20) && p.splits == 1) {
             const bool a8 = m <= 8;

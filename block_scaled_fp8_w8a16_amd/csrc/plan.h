@@ -16,28 +16,60 @@ constexpr uint32_t kDefaultCUs = 256;            // MI355X
 // Dynamic LDS a plan may use: the 160 KiB of a gfx950 CU less room for the
 // kernels' small static __shared__ variables.
 constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 256;
-constexpr uint32_t kTileRows = 128;              // tile kernel: rows of C per tile
 constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per split (one per lane)
 
-// LDS of the tile kernel for a 128 x (16 * n_blocks) C tile: a_stages
-// buffers of one K step of A (128 rows x 256 bytes of BF16), w_stages
-// buffers of one K step of the FP8 weight (16 * n_blocks rows x 128 bytes)
-// and the split's scale row (at most 64 floats).
-constexpr uint32_t tile_lds_bytes(uint32_t n_blocks, uint32_t w_stages, uint32_t a_stages)
+// LDS of the tile kernel for a (16 * m_blocks) x (16 * n_blocks) C tile:
+// a_stages buffers of one K step of A (16 * m_blocks rows x 256 bytes of
+// BF16), w_stages buffers of one K step of the FP8 weight (16 * n_blocks
+// rows x 128 bytes) and the split's scale row (at most 64 floats).
+constexpr uint32_t tile_lds_bytes(uint32_t m_blocks, uint32_t n_blocks, uint32_t w_stages,
+                                  uint32_t a_stages)
 {
-    return a_stages * kTileRows * 256 + w_stages * 16 * n_blocks * 128 + 256;
+    return a_stages * 16 * m_blocks * 256 + w_stages * 16 * n_blocks * 128 + 256;
+}
+
+// Built tile-kernel ring sizes (weight buffers = depth, A buffers =
+// a_depth) per tile shape; tiles are 64 or 128 rows by 64 or 128 columns.
+// The list is the dispatch table of the tile kernel's launcher.
+#define W8A16_TILE_VARIANTS(X)                                                        \
+    X(8, 4, 4, 2) X(8, 4, 6, 2) X(8, 4, 8, 2) X(8, 4, 4, 3) X(8, 4, 6, 3)             \
+    X(8, 8, 3, 2) X(8, 8, 4, 2) X(8, 8, 5, 2) X(8, 8, 3, 3)                           \
+    X(4, 4, 6, 2) X(4, 4, 8, 2) X(4, 4, 6, 3) X(4, 4, 8, 3) X(4, 4, 8, 4)             \
+    X(4, 4, 6, 5) X(4, 4, 4, 6) X(4, 4, 6, 6)                                         \
+    X(4, 8, 4, 2) X(4, 8, 6, 2) X(4, 8, 4, 3) X(4, 8, 6, 3) X(4, 8, 4, 4)             \
+    X(4, 8, 5, 4) X(4, 8, 4, 5) X(4, 8, 3, 5) X(4, 8, 3, 6)
+
+constexpr uint32_t tile_variant_key(uint32_t m_blocks, uint32_t n_blocks, uint32_t depth,
+                                    uint32_t a_depth)
+{
+    return ((m_blocks * 16 + n_blocks) * 16 + depth) * 16 + a_depth;
+}
+
+constexpr bool tile_depth_built(uint32_t m_blocks, uint32_t n_blocks, uint32_t depth,
+                                uint32_t a_depth)
+{
+#define W8A16_TILE_KEY_MATCH(MB, NB, D, AD) || key == tile_variant_key(MB, NB, D, AD)
+    const uint32_t key = tile_variant_key(m_blocks, n_blocks, depth, a_depth);
+    return false W8A16_TILE_VARIANTS(W8A16_TILE_KEY_MATCH);
+#undef W8A16_TILE_KEY_MATCH
 }
 
 // Tile kernel wave counts: 4 (one wave per SIMD), 8 (two groups splitting
 // every K step), and 6 or 10 (those plus two producer waves that only issue
 // the LDS DMA).  Variants that would spill registers are not built: with
 // producers, a SIMD holds three waves of the 8-wave layout (10 waves), which
-// fits only the 64-column tile, and the 6-wave 128-column tile fits only two
-// A buffers.
-constexpr bool tile_variant_ok(uint32_t n_blocks, uint32_t a_stages, uint32_t waves)
+// fits the 128-row tile only at 64 columns, and the 6-wave 128 x 128 tile
+// fits only two A buffers.  A producer wave waits on up to depth - 2 steps
+// of its ring (n_blocks * 2 loads each), which the 6-bit vmcnt must hold.
+constexpr bool tile_variant_ok(uint32_t m_blocks, uint32_t n_blocks, uint32_t depth,
+                               uint32_t a_stages, uint32_t waves)
 {
     if (waves == 4 || waves == 8)
         return true;
+    if (n_blocks * 2 * (depth - 2) > 63 || m_blocks * 4 * (a_stages - 2) > 63)
+        return false;
+    if (m_blocks == 4)
+        return waves == 6 || waves == 10;
     if (waves == 6)
         return n_blocks == 4 || a_stages == 2;
     if (waves == 10)

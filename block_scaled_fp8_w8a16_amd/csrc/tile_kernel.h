@@ -1,5 +1,7 @@
 // Tiled W8A16 GEMM kernel for large m (gfx950), plus the fixed-order
-// reduction of its K splits.
+// reduction of its K splits.  Included by tile_m64.hip and tile_m128.hip,
+// which instantiate the 64-row and the 128-row variants in separate
+// translation units (they build in parallel).
 //
 // Same operation as the stream kernel (page "w8a16_gemm_pipelined_m32.rs":
 // operand layouts in the doc comment of `w8a16_gemm_pipelined_m32_strided`,
@@ -8,10 +10,10 @@
 // shares the dequantized weight across all its rows
 // (`w8a16_gemm_pipelined_by_m`); this is that idea rebuilt for MI355X:
 //
-//   * A workgroup (4 waves, 2 x 2) owns a 128-row x NT-column tile of C over
-//     a range of 128-wide K steps.  Each wave owns 64 rows x NT/2 columns:
-//     4 x NT/32 MFMA 16x16x32 tiles.
-//   * Per K step the workgroup stages A (128 rows x 256 bytes of BF16) and
+//   * A workgroup (4 waves, 2 x 2) owns an MT-row x NT-column tile of C
+//     (MT, NT = 64 or 128) over a range of 128-wide K steps.  Each wave owns
+//     MT/2 rows x NT/2 columns: MT/32 x NT/32 MFMA 16x16x32 tiles.
+//   * Per K step the workgroup stages A (MT rows x 256 bytes of BF16) and
 //     the weight (NT rows x 128 bytes of FP8) straight from global memory
 //     into LDS with global_load_lds_dwordx4: the weight in a ring of WST
 //     buffers (WST - 1 steps ahead, to cover HBM latency), A in a ring of
@@ -42,6 +44,8 @@
 //   * Rows past m and columns past n are read from clamped, valid addresses
 //     and never stored.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,8 +59,6 @@ namespace {
 
 using namespace dev;
 
-constexpr uint32_t kTileM = 128;
-constexpr uint32_t kABytes = kTileM * 256;   // one K step of A in LDS
 
 // DMA one K step of A, or of the weight, of this wave's share into an LDS
 // buffer: loads u = 0..N-1 of the wave's group g, each one 1 KiB of LDS.
@@ -75,16 +77,16 @@ __device__ __forceinline__ void issue_ring(uint8_t *dst, uint32_t grp, uint32_t 
 // Producer-wave forms: the whole ring's loads of one step, each address
 // computed at issue (a producer has no math to overlap, and keeping 32
 // pointers live would cost the compute waves registers).  Same LDS image as
-// the shared forms: A load i fills plane i / 16, rows 8(i % 16)..+7; weight
+// the shared forms: A load i fills plane i / (MT/8), rows 8(i % (MT/8))..+7; weight
 // load i fills rows 8i..8i+7; lane s writes slot s % 8 of row s / 8.
-template <int N>
+template <int N, int MT>
 __device__ __forceinline__ void issue_a_all(uint8_t *dst, uint32_t t, const GemmArgs &g,
                                             uint32_t m0, uint32_t lane)
 {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const uint32_t plane = (uint32_t)i >> 4;
-        const uint32_t r = 8u * ((uint32_t)i & 15u) + (lane >> 3);
+        const uint32_t plane = (uint32_t)i / (MT / 8);
+        const uint32_t r = 8u * ((uint32_t)i % (MT / 8)) + (lane >> 3);
         const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
         const uint32_t row = min(m0 + r, g.m - 1u);
         __builtin_amdgcn_global_load_lds(g.a + (size_t)row * g.a_stride * 2u + c * 16u + t * 256u,
@@ -120,11 +122,13 @@ __device__ __forceinline__ void wait_vm_ahead(uint32_t ahead)
     }
 }
 
-template <int NT, int WST, int AST, int KH, bool PROD>
+template <int MT, int NT, int WST, int AST, int KH, bool PROD>
 __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_kernel(GemmArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr uint32_t kABytes = MT * 256;   // one K step of A in LDS
     constexpr uint32_t kWBytes = NT * 128;
+    constexpr int MBW = MT / 32;             // 16-row blocks per wave
     constexpr uint32_t CW = 4 * KH;          // compute waves
     // Loads per issuing wave per step: with PROD one producer wave issues a
     // whole ring, else the even compute waves share the weight ring and the
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
     const uint32_t tile = lid / g.splits;
     const uint32_t m_tile = tile % g.m_tiles;
     const uint32_t n_tile = tile / g.m_tiles;
-    const uint32_t m0 = m_tile * kTileM;
+    const uint32_t m0 = m_tile * MT;
     const uint32_t n0 = n_tile * NT;
     const uint32_t ksteps = g.k / 128u;
     const uint32_t s0 = split * g.steps_per_split;
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
     auto phys = [](uint32_t t) { return t; };
 
     // ---- DMA sources.  In LDS, A is two planes (K-step bytes 0..127 and
-    // 128..255 of each row), each 128 rows x 128 bytes; the weight is NT rows
+    // 128..255 of each row), each MT rows x 128 bytes; the weight is NT rows
     // x 128 bytes.  Within a 128-byte row r, slot p holds 16-byte chunk
     // p ^ wswz(r % 16): with rows 128 bytes apart this makes the MFMA operand
     // reads below (16 lanes = 16 consecutive rows, one chunk each) free of
@@ -182,9 +186,9 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
         if (PROD || !issues) {
             src[u] = g.w;
         } else if (!wrole && u < NA) {
-            const uint32_t i = grp * NA + u;          // 0..31: plane i / 16, rows 8(i % 16)..+7
-            const uint32_t plane = i >> 4;
-            const uint32_t r = 8u * (i & 15u) + (lane >> 3);
+            const uint32_t i = grp * NA + u;          // plane i / (MT/8), rows 8(i % (MT/8))..+7
+            const uint32_t plane = i / (MT / 8);
+            const uint32_t r = 8u * (i % (MT / 8)) + (lane >> 3);
             const uint32_t c = 8u * plane + ((lane & 7u) ^ wswz(r & 15u));
             const uint32_t row = min(m0 + r, g.m - 1u);
             src[u] = g.a + (size_t)row * g.a_stride * 2u + c * 16u;
@@ -205,13 +209,14 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
     // With KH == 2 the two groups of four waves take k-quarters 0-1 and 2-3
     // of every step over the same staged buffers, so each SIMD runs two
     // waves: one wave's LDS and barrier waits overlap the other's MFMAs.
-    uint32_t aoff[4][QW];
+    uint32_t aoff[MBW][QW];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < MBW; ++b)
 #pragma unroll
         for (int qq = 0; qq < QW; ++qq) {
             const uint32_t q = kh * QW + qq;
-            aoff[b][qq] = ((4u * gq + q) >> 3) * (kTileM * 128u) + (64u * wm + 16u * b + rr) * 128u +
+            aoff[b][qq] = ((4u * gq + q) >> 3) * (MT * 128u) +
+                          ((MT / 2) * wm + 16u * b + rr) * 128u +
                           ((((4u * gq + q) & 7u) ^ wswz(rr)) * 16u);
         }
     uint32_t woff[NBW][HW];
@@ -223,11 +228,11 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
             woff[j][hh] = ((NT / 2) * wn + 16u * j + rr) * 128u +
                           (((2u * gq + h) ^ wswz(rr)) * 16u);
         }
-    f32x4_t acc[NBW][4];
+    f32x4_t acc[NBW][MBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < MBW; ++b)
             acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Prologue.  Wave 1 first moves the scales of the tile's 128-row block
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
         for (int st = 0; st < AST - 1; ++st)
             if (s0 + st < s1) {
                 if constexpr (PROD)
-                    issue_a_all<NA>(abuf + st * kABytes, phys(s0 + st), g, m0, lane);
+                    issue_a_all<NA, MT>(abuf + st * kABytes, phys(s0 + st), g, m0, lane);
                 else
                     issue_ring<NA, 256u>(abuf + st * kABytes, grp, phys(s0 + st), src);
             }
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
                 if (t + AST - 1 < s1) {
                     uint8_t *dst = abuf + ((idx + AST - 1) % AST) * kABytes;
                     if constexpr (PROD)
-                        issue_a_all<NA>(dst, phys(t + AST - 1), g, m0, lane);
+                        issue_a_all<NA, MT>(dst, phys(t + AST - 1), g, m0, lane);
                     else
                         issue_ring<NA, 256u>(dst, grp, phys(t + AST - 1), src);
                 }
@@ -302,12 +307,12 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
 #pragma unroll
             for (int hh = 0; hh < HW; ++hh)
                 wraw[j][hh] = *reinterpret_cast<const u32x4_t *>(sw + woff[j][hh]);
-        f32x4_t p[NBW][4];
+        f32x4_t p[NBW][MBW];
 #pragma unroll
         for (int qq = 0; qq < QW; ++qq) {
-            bf16x8_t af[4];
+            bf16x8_t af[MBW];
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < MBW; ++b)
                 af[b] = *reinterpret_cast<const bf16x8_t *>(sa + aoff[b][qq]);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
                 dequant16(wraw[j][qq >> 1], lo, hi);
                 const bf16x8_t wb = (qq & 1) ? hi : lo;
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < MBW; ++b)
                     p[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         wb, af[b], qq == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : p[j][b], 0, 0, 0);
             }
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < MBW; ++b) {
                 acc[j][b].x = __builtin_fmaf(s, p[j][b].x, acc[j][b].x);
                 acc[j][b].y = __builtin_fmaf(s, p[j][b].y, acc[j][b].y);
                 acc[j][b].z = __builtin_fmaf(s, p[j][b].z, acc[j][b].z);
@@ -335,14 +340,14 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
     // LDS (every wave has waited for all its loads: the last step waits for
     // none outstanding), and the first adds them: acc = group 0 + group 1.
     if constexpr (KH == 2) {
-        f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);   // [4 waves][NBW][4][64]
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);   // [4 waves][NBW][MBW][64]
         barrier_lds();
         if (computes && kh == 1) {
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    red[(((wave & 3u) * NBW + j) * 4 + b) * 64 + lane] = acc[j][b];
+                for (int b = 0; b < MBW; ++b)
+                    red[(((wave & 3u) * NBW + j) * MBW + b) * 64 + lane] = acc[j][b];
         }
         barrier_lds();
         if (!computes || kh == 1)
@@ -350,30 +355,30 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[j][b] += red[((wave * NBW + j) * 4 + b) * 64 + lane];
+            for (int b = 0; b < MBW; ++b)
+                acc[j][b] += red[((wave * NBW + j) * MBW + b) * 64 + lane];
     }
 
     if (!computes)
         return;
     // ---- epilogue: lane holds C[row][col..col+3] of each (j, b) tile.
-    const uint32_t row_off = 64u * wm + rr;
+    const uint32_t row_off = (MT / 2) * wm + rr;
     const uint32_t col_off = (NT / 2) * wn + 4u * gq;
     if (g.splits == 1) {
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < MBW; ++b)
                 store_c4(g, acc[j][b], m0 + row_off + 16u * b, n0 + col_off + 16u * j);
         return;
     }
-    // Workspace [splits][m_tiles * 128][n_tiles * NT] FP32, whole tiles.
+    // Workspace [splits][m_tiles * MT][n_tiles * NT] FP32, whole tiles.
     const size_t ws_cols = (size_t)g.n_tiles * NT;
-    float *wsp = g.ws + ((size_t)split * g.m_tiles * kTileM) * ws_cols;
+    float *wsp = g.ws + ((size_t)split * g.m_tiles * MT) * ws_cols;
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < MBW; ++b)
             *reinterpret_cast<f32x4_t *>(wsp + (size_t)(m0 + row_off + 16u * b) * ws_cols + n0 +
                                          col_off + 16u * j) = acc[j][b];
 }
@@ -397,14 +402,15 @@ __global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uin
     store_c4(g, s, row, col);
 }
 
-template <int NT, int WST, int AST, int KH, bool PROD>
+template <int MT, int NT, int WST, int AST, int KH, bool PROD>
 hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    if constexpr (!tile_variant_ok(NT / 16, AST, 4 * KH + (PROD ? 2 : 0))) {
+    if constexpr (!tile_variant_ok(MT / 16, NT / 16, WST, AST, 4 * KH + (PROD ? 2 : 0)) ||
+                  !tile_depth_built(MT / 16, NT / 16, WST, AST)) {
         (void)g, (void)p, (void)stream;
         return hipErrorInvalidValue;
     } else {
-    auto kern = w8a16_tile_kernel<NT, WST, AST, KH, PROD>;
+    auto kern = w8a16_tile_kernel<MT, NT, WST, AST, KH, PROD>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -419,7 +425,7 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
     if (e != hipSuccess || p.splits == 1)
         return e;
     const uint32_t ws_cols = p.n_tiles * NT;
-    const uint32_t ws_rows = p.m_tiles * kTileM;
+    const uint32_t ws_rows = p.m_tiles * MT;
     const uint64_t threads = (uint64_t)g.m * (ws_cols / 4u);
     const uint32_t blocks = (uint32_t)((threads + 255u) / 256u);
     hipLaunchKernelGGL(w8a16_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, g, ws_cols,
@@ -428,35 +434,37 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
     }
 }
 
-template <int NT, int WST, int AST>
+template <int MT, int NT, int WST, int AST>
 hipError_t launch_tile_k(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     switch (p.waves) {
-    case 4: return launch_tile_t<NT, WST, AST, 1, false>(g, p, stream);
-    case 6: return launch_tile_t<NT, WST, AST, 1, true>(g, p, stream);
-    case 8: return launch_tile_t<NT, WST, AST, 2, false>(g, p, stream);
-    case 10: return launch_tile_t<NT, WST, AST, 2, true>(g, p, stream);
+    case 4: return launch_tile_t<MT, NT, WST, AST, 1, false>(g, p, stream);
+    case 6: return launch_tile_t<MT, NT, WST, AST, 1, true>(g, p, stream);
+    case 8: return launch_tile_t<MT, NT, WST, AST, 2, false>(g, p, stream);
+    case 10: return launch_tile_t<MT, NT, WST, AST, 2, true>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_tile(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+// Launch of the variant a (validated) plan names, for the tiles with
+// m_blocks == MB; the table rows of other heights are compiled out.
+template <uint32_t MB>
+hipError_t launch_tile_rows(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    const int ast = (p.flags & W8A16_FLAG_A3) ? 3 : 2;
-    switch (p.n_blocks * 100 + p.depth * 10 + ast) {
-    case 442: return launch_tile_k<64, 4, 2>(g, p, stream);
-    case 462: return launch_tile_k<64, 6, 2>(g, p, stream);
-    case 482: return launch_tile_k<64, 8, 2>(g, p, stream);
-    case 443: return launch_tile_k<64, 4, 3>(g, p, stream);
-    case 463: return launch_tile_k<64, 6, 3>(g, p, stream);
-    case 832: return launch_tile_k<128, 3, 2>(g, p, stream);
-    case 842: return launch_tile_k<128, 4, 2>(g, p, stream);
-    case 852: return launch_tile_k<128, 5, 2>(g, p, stream);
-    case 833: return launch_tile_k<128, 3, 3>(g, p, stream);
+    const uint32_t key = tile_variant_key(p.m_blocks, p.n_blocks, p.depth, p.a_depth);
+#define W8A16_TILE_CASE(MB_, NB, D, AD)                                               \
+    case tile_variant_key(MB_, NB, D, AD):                                            \
+        if constexpr (MB_ == MB)                                                      \
+            return launch_tile_k<16 * MB_, 16 * NB, D, AD>(g, p, stream);             \
+        else                                                                          \
+            return hipErrorInvalidValue;
+    switch (key) {
+    W8A16_TILE_VARIANTS(W8A16_TILE_CASE)
     default: return hipErrorInvalidValue;
     }
+#undef W8A16_TILE_CASE
 }
 
 }  // namespace w8a16

@@ -66,9 +66,10 @@ typedef enum w8a16_kernel {
      * K steps, and K may be split across workgroups with a fixed-order
      * FP32 fix-up. */
     W8A16_KERNEL_STREAM = 1,
-    /* Tiled kernel for large m: a workgroup owns a 128-row x n_blocks*16
-     * column tile of C, shares the A and dequantized W tiles of each K step
-     * through LDS, and its waves split the tile, not K. */
+    /* Tiled kernel for m above 32: a workgroup owns a 16*m_blocks-row
+     * (64 or 128) x 16*n_blocks-column (64 or 128) tile of C, stages A and
+     * the FP8 weight of each K step in LDS rings (a_depth and depth
+     * buffers), and its waves split the tile (8 waves: also each K step). */
     W8A16_KERNEL_TILE = 2,
     /* Ring kernel for small m: a workgroup owns n_blocks 16-column blocks
      * and m_blocks 16-row blocks of C over all of K, streams K in stages of
@@ -79,7 +80,8 @@ typedef enum w8a16_kernel {
 } w8a16_kernel;
 
 /* Launch plan.  w8a16_plan() fills every field; callers may change
- * kernel, m_blocks, n_blocks, splits, depth, flags, waves and stage_steps and pass the result to
+ * kernel, m_blocks, n_blocks, splits, depth, flags, waves, stage_steps and
+ * a_depth and pass the result to
  * w8a16_gemm_planned(), which recomputes the derived fields and rejects a
  * plan the kernels do not support (W8A16_ERR_BAD_PLAN). */
 typedef struct w8a16_plan {
@@ -99,8 +101,10 @@ typedef struct w8a16_plan {
     uint32_t depth;           /* stream: K steps each wave keeps in flight (1, 2, 4);
                                  tile: weight ring buffers; ring: stages in flight (2..4) */
     uint32_t flags;           /* W8A16_FLAG_* bits */
-    uint32_t waves;           /* waves per workgroup (stream 4/8/16, ring 8/16, tile 4) */
+    uint32_t waves;           /* waves per workgroup (stream 4/8/16, ring 8/16,
+                                 tile 4/6/8/10) */
     uint32_t stage_steps;     /* ring: K steps per stage (4 or 8); 0 for the others */
+    uint32_t a_depth;         /* tile: A ring buffers (2..6; 0 means 2); 0 for the others */
 } w8a16_plan_t;
 
 /* Plan flags. */
@@ -111,9 +115,7 @@ enum {
     W8A16_FLAG_DIRECT = 1u,
     /* Ring kernel, m <= 8 with m_blocks == 1: stage 8 A rows instead of 16
      * (derived by w8a16_plan_finalize from m; callers need not set it). */
-    W8A16_FLAG_A8 = 2u,
-    /* Tile kernel: three A buffers (A two steps ahead) instead of two. */
-    W8A16_FLAG_A3 = 4u
+    W8A16_FLAG_A8 = 2u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

@@ -102,12 +102,12 @@ def _covers(p: Plan, m, n, k):
 def test_default_plans_cover_the_problem(m, n, k):
     p = w8.plan(m, n, k)
     _covers(p, m, n, k)
-    assert p.block in (256, 512, 1024)
+    assert p.block in (256, 384, 512, 640, 1024)
     assert p.lds_bytes <= 160 * 1024
     if p.splits > 1 and p.kernel == w8.KERNEL_TILE:
         # whole FP32 tiles per split; no arrival counters (second kernel)
-        assert p.workspace_bytes == (p.splits * p.m_tiles * 128 * p.n_tiles * 16 *
-                                     p.n_blocks * 4)
+        assert p.workspace_bytes == (p.splits * p.m_tiles * 16 * p.m_blocks * p.n_tiles *
+                                     16 * p.n_blocks * 4)
         assert p.counter_count == 0
     elif p.splits > 1:
         assert p.workspace_bytes == p.grid * p.m_blocks * p.n_blocks * 1024
@@ -167,11 +167,13 @@ def test_ring_plans():
 def test_large_m_plans_tile_kernel():
     p = w8.plan(128, 8192, 8192)
     assert p.kernel == w8.KERNEL_TILE
-    assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (8, 8, 4, 16)
-    assert p.grid == 256 and p.counter_count == 0
-    assert p.workspace_bytes == 4 * 128 * 8192 * 4
-    assert p.lds_bytes == 2 * 128 * 256 + p.depth * 128 * 128 + 256 <= 160 * 1024 - 256
-    p3 = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 8, 4, depth=3, flags=w8.FLAG_A3,
+    # two 64-row tiles x 64 128-column tiles x 2 splits: one workgroup per CU
+    assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (4, 8, 2, 32)
+    assert (p.m_tiles, p.grid, p.counter_count) == (2, 256, 0)
+    assert p.workspace_bytes == 2 * 128 * 8192 * 4
+    assert p.lds_bytes == p.a_depth * 64 * 256 + p.depth * 128 * 128 + 256
+    assert p.lds_bytes <= 160 * 1024 - 256
+    p3 = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 8, 4, depth=3, a_depth=3,
                       waves=4)
     assert p3.lds_bytes == 3 * 128 * 256 + 3 * 128 * 128 + 256
     # a split may not exceed 64 K steps (one scale per lane)
@@ -185,25 +187,48 @@ def test_large_m_plans_tile_kernel():
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 4, 1, depth=5, waves=4)
     with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 2, 8, 1, depth=3, waves=4)
+    with pytest.raises(w8.W8A16Error):      # 64-row tiles: weight buffers 4 or 6
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 4, 8, 1, depth=3, waves=4)
+    with pytest.raises(w8.W8A16Error):      # a producer wave's vmcnt holds 4 x 16 loads at most
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 4, 8, 1, depth=6, waves=6)
     with pytest.raises(w8.W8A16Error):      # three A buffers leave room for 3 weight buffers
-        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=4, flags=w8.FLAG_A3,
+        w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=4, a_depth=3,
                      waves=4)
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 256, 1024, w8.KERNEL_TILE, 8, 8, 1, depth=3, flags=w8.FLAG_A8,
                      waves=4)
 
 
-def test_large_m_prefers_64_column_tiles_over_short_splits():
-    # 128-column tiles would need 8 splits of 4 K steps; 64-column tiles
-    # fill the chip with 4 splits of 8 steps
+def test_64_row_tiles():
+    p = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 4, 8, 2, depth=6, a_depth=3,
+                     waves=8)
+    assert (p.m_tiles, p.n_tiles, p.grid, p.steps_per_split) == (2, 64, 256, 32)
+    assert p.lds_bytes == 3 * 64 * 256 + 6 * 128 * 128 + 256
+    assert p.workspace_bytes == 2 * 128 * 8192 * 4
+    p = w8.make_plan(40, 1000, 1024, w8.KERNEL_TILE, 4, 4, 1, depth=8, waves=10)
+    assert (p.m_tiles, p.n_tiles, p.block) == (1, 16, 640)
+    assert p.lds_bytes == 2 * 64 * 256 + 8 * 64 * 128 + 256
+    _covers(p, 40, 1000, 1024)
+
+
+def test_tile_plans_fill_the_cus_with_long_splits():
+    # 128-column tiles would need 4 splits of 8 K steps; 64-column tiles
+    # fill the chip with 2 splits of 16 steps
     p = w8.plan(96, 4096, 4096)
-    assert (p.kernel, p.n_blocks, p.splits, p.steps_per_split) == (w8.KERNEL_TILE, 4, 4, 8)
+    assert (p.kernel, p.m_blocks, p.n_blocks, p.splits, p.steps_per_split, p.grid) == \
+        (w8.KERNEL_TILE, 4, 4, 2, 16, 256)
     _covers(p, 96, 4096, 4096)
-    p = w8.plan(256, 4096, 4096)       # two row tiles: 4 splits of 8 steps already
-    assert (p.n_blocks, p.splits) == (8, 4)
-    p = w8.plan(128, 8192, 8192)
-    assert (p.n_blocks, p.splits, p.waves) == (8, 4, 8)
+    # 128-column tiles with 16-step splits
+    p = w8.plan(48, 8192, 8192)
+    assert (p.kernel, p.m_blocks, p.n_blocks, p.splits, p.grid) == (w8.KERNEL_TILE, 4, 8, 4, 256)
+    # above 128 rows, 128-row tiles
+    p = w8.plan(256, 4096, 4096)
+    assert (p.m_blocks, p.m_tiles, p.n_blocks, p.splits, p.grid) == (8, 2, 4, 2, 256)
+    # 33..64 rows over a weight of at most 16 MiB stream
+    assert w8.plan(48, 4096, 4096).kernel == w8.KERNEL_STREAM
+    assert w8.plan(64, 6144, 2048).kernel == w8.KERNEL_STREAM
+    assert w8.plan(33, 8192, 4096).kernel == w8.KERNEL_TILE
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():

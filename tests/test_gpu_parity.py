@@ -11,6 +11,7 @@ import pytest
 
 import datagen
 import oracle
+from variants import tile_variants
 
 pytestmark = pytest.mark.gpu
 
@@ -199,22 +200,21 @@ def test_ring_kernel_strides_and_short_k(w8):
         assert ran >= 2
 
 
-TILE_VARIANTS = [(8, 3, 0), (8, 4, 0), (8, 5, 0), (8, 3, 4), (4, 4, 0), (4, 6, 0), (4, 8, 0),
-                 (4, 4, 4), (4, 6, 4)]
+TILE_VARIANTS = tile_variants()
 
 
-@pytest.mark.parametrize("nb,depth,flags", TILE_VARIANTS)
+@pytest.mark.parametrize("mb,nb,depth,a_depth", TILE_VARIANTS)
 @pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("m", [65, 128, 200])
+@pytest.mark.parametrize("m", [40, 128, 200])
 @pytest.mark.parametrize("waves", [4, 6, 8, 10])
-def test_exact_data_every_tile_variant(w8, nb, depth, flags, splits, m, waves):
+def test_exact_data_every_tile_variant(w8, mb, nb, depth, a_depth, splits, m, waves):
     """K long enough for both rings to wrap, in every split; 8 waves split
     every K step between two groups; 6 and 10 add two producer waves."""
     n, k = 16 * nb * 3 + 7, 128 * 23
-    p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits + flags + waves)
+    p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits + a_depth + waves + mb)
     try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, nb, splits, depth=depth, flags=flags,
-                            waves=waves)
+        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, mb, nb, splits, depth=depth,
+                            a_depth=a_depth, waves=waves)
     except w8.W8A16Error as e:
         assert e.status == w8.ERR_BAD_PLAN and "wave variant" in str(e)
         pytest.skip("variant not built: %s" % e)
@@ -226,10 +226,13 @@ def test_exact_data_every_tile_variant(w8, nb, depth, flags, splits, m, waves):
 def test_tile_kernel_long_k_and_strides(w8):
     p = datagen.make_problem(130, 300, 128 * 40, seed=21, a_row_stride=128 * 40 + 24,
                              c_row_stride=311, c_extra_rows=2)
-    for nb, depth, splits, flags, waves in [(8, 5, 1, 0, 4), (8, 3, 4, 4, 8), (4, 6, 5, 0, 8),
-                                            (4, 4, 2, 4, 4), (8, 4, 3, 0, 6), (4, 6, 2, 4, 10)]:
-        plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_TILE, 8, nb, splits, depth=depth,
-                            flags=flags, waves=waves)
+    for mb, nb, depth, splits, a_depth, waves in [
+            (8, 8, 5, 1, 2, 4), (8, 8, 3, 4, 3, 8), (8, 4, 6, 5, 2, 8), (8, 4, 4, 2, 3, 4),
+            (8, 8, 4, 3, 2, 6), (8, 4, 6, 2, 3, 10), (4, 8, 6, 1, 2, 8), (4, 8, 4, 2, 3, 10),
+            (4, 4, 8, 3, 3, 6), (4, 4, 6, 1, 2, 4), (4, 8, 3, 2, 6, 8), (4, 8, 4, 3, 5, 4),
+            (4, 4, 6, 1, 6, 8), (4, 4, 8, 2, 4, 10)]:
+        plan = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_TILE, mb, nb, splits, depth=depth,
+                            a_depth=a_depth, waves=waves)
         g = run_gpu(w8, p, plan)
         check_full(p, g)
         assert np.array_equal(g, run_gpu(w8, p, plan))
