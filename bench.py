@@ -18,6 +18,7 @@ Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only-main]
     python bench.py --traffic-run          (workload for rocprofv3 --pmc runs)
     python bench.py --m-sweep N K          (default plan for m = 1..256, one line each)
+    python bench.py --batched              (Q/K/V arms in one batched call vs three calls)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 
@@ -329,7 +330,107 @@ def m_sweep(n: int, k: int, steps: int = 50):
                           "plan": plan.as_dict(), "output_sane": ok}), flush=True)
 
 
+QKV_ARMS = (4096, 1024, 1024)      # Q, K, V output widths (grouped K/V heads)
+
+
+def batched_bench(m: int = 8, k: int = 4096, steps: int = 100, warmup: int = 10):
+    """The batched tier on decode-size Q/K/V arms sharing one A (m rows,
+    hidden k): one w8a16_gemm_batched call per step against the same arms
+    as three w8a16_gemm calls, both cold (replicas over >= 512 MiB) and in
+    graph replay.  Prints one JSON line."""
+    import numpy as np
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    w8.library()
+    probs = [datagen.make_problem(m, n, k, seed=8000 + i) for i, n in enumerate(QKV_ARMS)]
+    per = probs[0].a.nbytes + sum(p.w.nbytes + p.scale.nbytes + p.c.nbytes for p in probs)
+    reps = max(1, -(-ARENA_BYTES // per))
+    dev = torch.device("cuda")
+    a = torch.from_numpy(probs[0].a).view(torch.int16).to(dev).reshape(1, -1).repeat(reps, 1)
+    arms = []
+    for p in probs:
+        w = torch.from_numpy(p.w).to(dev).reshape(1, -1).repeat(reps, 1)
+        sc = torch.from_numpy(p.scale).to(dev).reshape(1, -1).repeat(reps, 1)
+        c = torch.from_numpy(p.c).view(torch.int16).to(dev).reshape(1, -1).repeat(reps, 1)
+        arms.append((p, w, sc, c))
+
+    def descs(i):
+        r = i % reps
+        return [dict(a=a[r].data_ptr(), w_fp8=w[r].data_ptr(), block_scale=sc[r].data_ptr(),
+                     c=c[r].data_ptr(), a_row_stride=k, c_row_stride=p.n, m=m, n=p.n, k=k)
+                for (p, w, sc, c) in arms]
+
+    stream = torch.cuda.Stream()
+
+    def batched(i):
+        st = w8.gemm_batched_raw(descs(i), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(w8.last_error())
+
+    def separate(i):
+        for d in descs(i):
+            st = w8.gemm_raw(d["a"], k, d["w_fp8"], d["block_scale"], d["c"], d["n"], m,
+                             d["n"], k, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(w8.last_error())
+
+    def graph_ms(fn):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    fn(warmup + i)
+            g.replay()
+            torch.cuda.synchronize()
+            start.record(stream)
+            g.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    ms_sep = graph_ms(separate)
+    ms_b = graph_ms(batched)
+    ok = True
+    for (p, w, sc, c) in arms:
+        for r in range(min(reps, steps + warmup)):
+            cc = c[r].cpu().numpy().view(np.uint16).reshape(p.c.shape)
+            ok &= bool(((cc[:m, :p.n] & 0x7F80) != 0x7F80).all())
+    nbytes = sum(p.n * k + 4 * (-(-p.n // 128)) * (k // 128) + 2 * m * k + 2 * m * p.n
+                 for p in probs)
+    flops = sum(2.0 * m * p.n * k for p in probs)
+    plan = w8.plan_batched([(m, n, k) for n in QKV_ARMS],
+                           torch.cuda.get_device_properties(0).multi_processor_count)
+    gbs = nbytes / (ms_b * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms_b, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qkv_batched_m%d_k%d_n%s" % (m, k, "_".join(map(str, QKV_ARMS))),
+                   "m": m, "k": k, "arms_n": list(QKV_ARMS), "shared_a": True,
+                   "weights": "cold", "arena_replicas": reps},
+        "us_per_call": round(ms_b * 1e3, 3),
+        "us_per_call_separate_calls": round(ms_sep * 1e3, 3),
+        "speedup_vs_separate": round(ms_sep / ms_b, 3),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tflops": round(flops / (ms_b * 1e-3) / 1e12, 3),
+        "plan": plan.as_dict(), "output_sane": ok,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "w8a16_stream_batched_kernel",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "kernel_source_hash": kernel_source_hash(), "note": NOTE}), flush=True)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--batched":
+        batched_bench()
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--m-sweep":
         n = int(sys.argv[2]) if len(sys.argv) > 2 else 8192
         k = int(sys.argv[3]) if len(sys.argv) > 3 else 8192

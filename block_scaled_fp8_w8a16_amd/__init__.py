@@ -40,7 +40,10 @@ FLAG_A8 = 2
 
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
-           "w8a16_gemm_planned", "w8a16_status_string", "w8a16_last_error")
+           "w8a16_gemm_planned", "w8a16_plan_batched", "w8a16_gemm_batched",
+           "w8a16_status_string", "w8a16_last_error")
+
+MAX_BATCH = 8
 
 
 class W8A16Error(RuntimeError):
@@ -63,6 +66,15 @@ class Plan(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+class GemmDesc(ctypes.Structure):
+    """One GEMM of a batched call (w8a16_gemm_desc_t): device addresses and
+    the w8a16_gemm() scalars."""
+    _fields_ = [("a", ctypes.c_void_p), ("w_fp8", ctypes.c_void_p),
+                ("block_scale", ctypes.c_void_p), ("c", ctypes.c_void_p),
+                ("a_row_stride", ctypes.c_uint32), ("c_row_stride", ctypes.c_uint32),
+                ("m", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32)]
 
 
 _lib = None
@@ -89,6 +101,11 @@ def library() -> ctypes.CDLL:
         lib.w8a16_gemm_planned.argtypes = [vp, u32, vp, vp, vp, u32, u32, u32, u32,
                                            ctypes.POINTER(Plan), vp]
         lib.w8a16_gemm_planned.restype = ctypes.c_int
+        lib.w8a16_plan_batched.argtypes = [ctypes.POINTER(GemmDesc), u32, u32,
+                                           ctypes.POINTER(Plan)]
+        lib.w8a16_plan_batched.restype = ctypes.c_int
+        lib.w8a16_gemm_batched.argtypes = [ctypes.POINTER(GemmDesc), u32, vp]
+        lib.w8a16_gemm_batched.restype = ctypes.c_int
         lib.w8a16_status_string.argtypes = [ctypes.c_int]
         lib.w8a16_status_string.restype = ctypes.c_char_p
         lib.w8a16_last_error.argtypes = []
@@ -186,3 +203,60 @@ def gemm(a, w, scale, c=None, *, plan_: Optional[Plan] = None, stream=None):
                   c_rs, m, n, k, stream.cuda_stream, plan_)
     _raise_if(st)
     return c
+
+
+def _desc_array(descs):
+    arr = (GemmDesc * max(1, len(descs)))()
+    for i, d in enumerate(descs):
+        arr[i] = d if isinstance(d, GemmDesc) else GemmDesc(**d)
+    return arr
+
+
+def plan_batched(shapes, cu_count: int = 0) -> Plan:
+    """Plan of a batched call for [(m, n, k), ...] (no GPU call)."""
+    descs = [GemmDesc(m=m, n=n, k=k) for (m, n, k) in shapes]
+    p = Plan()
+    _raise_if(library().w8a16_plan_batched(_desc_array(descs), len(descs), cu_count,
+                                           ctypes.byref(p)))
+    return p
+
+
+def gemm_batched_raw(descs, stream: int = 0) -> int:
+    """Direct call of w8a16_gemm_batched with GemmDesc (or dict) entries;
+    returns the status."""
+    return int(library().w8a16_gemm_batched(_desc_array(descs), len(descs), stream))
+
+
+def gemm_batched(problems, *, stream=None):
+    """Several independent GEMMs in one launch.  problems: a list of
+    (a, w, scale, c) tuples of CUDA tensors laid out as for gemm() (c is
+    required here).  Returns the list of c tensors."""
+    import torch
+    descs = []
+    for a, w, scale, c in problems:
+        if a.dim() != 2 or w.dim() != 2 or c.dim() != 2:
+            raise ValueError("a, w and c must be 2-D")
+        m, k = a.shape
+        n = w.shape[0]
+        if w.shape[1] != k or tuple(c.shape) != (m, n):
+            raise ValueError("shapes must be a [m, k], w [n, k], c [m, n]")
+        if a.dtype != torch.bfloat16 or a.stride(1) != 1:
+            raise ValueError("a must be bfloat16 with unit column stride")
+        if w.dtype not in (torch.uint8, torch.float8_e4m3fn) or not w.is_contiguous():
+            raise ValueError("w must be contiguous float8_e4m3fn or uint8")
+        if scale.dtype != torch.float32 or not scale.is_contiguous():
+            raise ValueError("scale must be contiguous float32")
+        if c.dtype != torch.bfloat16 or c.stride(1) != 1:
+            raise ValueError("c must be bfloat16 with unit column stride")
+        for t in (a, w, scale, c):
+            if not t.is_cuda:
+                raise ValueError("all operands must be GPU tensors")
+        descs.append(GemmDesc(a=a.data_ptr(), w_fp8=w.data_ptr(), block_scale=scale.data_ptr(),
+                              c=c.data_ptr(),
+                              a_row_stride=a.stride(0) if m > 1 else max(a.stride(0), k),
+                              c_row_stride=c.stride(0) if m > 1 else max(c.stride(0), n),
+                              m=m, n=n, k=k))
+    if stream is None:
+        stream = torch.cuda.current_stream(problems[0][0].device)
+    _raise_if(gemm_batched_raw(descs, stream.cuda_stream))
+    return [p[3] for p in problems]

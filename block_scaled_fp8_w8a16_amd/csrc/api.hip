@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -203,6 +204,70 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
         return st;
     return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, p,
                static_cast<hipStream_t>(stream));
+}
+
+int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream)
+{
+    using namespace w8a16;
+    if (!descs)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_gemm_batched: null descriptors");
+    if (count < 1 || count > W8A16_MAX_BATCH) {
+        char buf[128];
+        snprintf(buf, sizeof buf, "w8a16_gemm_batched: count=%u must be in 1..%u", count,
+                 (unsigned)W8A16_MAX_BATCH);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    for (uint32_t i = 0; i < count; ++i) {
+        const w8a16_gemm_desc_t &d = descs[i];
+        int st = check_call(d.a, d.a_row_stride, d.w_fp8, d.block_scale, d.c, d.c_row_stride,
+                            d.m, d.n, d.k);
+        if (st != W8A16_OK)
+            return fail_at(st, i);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    uint32_t cus = 0;
+    int st = device_cu_count(dev, &cus);
+    if (st != W8A16_OK)
+        return st;
+    w8a16_plan_t plan;
+    st = plan_batched(descs, count, cus, &plan);
+    if (st != W8A16_OK)
+        return st;
+    BatchArgs b;
+    std::memset(&b, 0, sizeof b);
+    b.count = count;
+    uint32_t start = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+        const w8a16_gemm_desc_t &d = descs[i];
+        GemmArgs &g = b.g[i];
+        g.a = static_cast<const uint8_t *>(d.a);
+        g.w = static_cast<const uint8_t *>(d.w_fp8);
+        g.scale = d.block_scale;
+        g.c = static_cast<uint8_t *>(d.c);
+        g.ws = nullptr;
+        g.counters = nullptr;
+        g.a_stride = d.a_row_stride;
+        g.c_stride = d.c_row_stride;
+        g.m = d.m;
+        g.n = d.n;
+        g.k = d.k;
+        g.m_tiles = (d.m + 16 * plan.m_blocks - 1) / (16 * plan.m_blocks);
+        g.n_tiles = (d.n + 16 * plan.n_blocks - 1) / (16 * plan.n_blocks);
+        g.splits = 1;
+        g.steps_per_split = d.k / kKStep;
+        b.start[i] = start;
+        start += g.m_tiles * g.n_tiles;
+    }
+    if (start != plan.grid)
+        return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_batched: inconsistent grid");
+    e = launch_stream_batched(b, plan, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    set_last_error("");
+    return W8A16_OK;
 }
 
 }  // extern "C"

@@ -23,7 +23,16 @@ struct GemmArgs {
     uint32_t m_tiles, n_tiles, splits, steps_per_split;
 };
 
+// Up to W8A16_MAX_BATCH GEMMs in one grid of the stream kernel: problem i
+// owns logical workgroups start[i] .. start[i + 1] - 1 (start[0] == 0).
+struct BatchArgs {
+    GemmArgs g[W8A16_MAX_BATCH];
+    uint32_t start[W8A16_MAX_BATCH];
+    uint32_t count;
+};
+
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_stream_batched(const BatchArgs &b, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m64(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m128(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_ring(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);

@@ -381,9 +381,104 @@ const char *status_string(int status)
     }
 }
 
+// Prefix the thread's last error with the index of the descriptor it came
+// from and return `status`.
+int fail_at(int status, uint32_t index)
+{
+    char buf[320];
+    const char *msg = last_error();
+    snprintf(buf, sizeof buf, "w8a16_gemm_batched: descriptor %u: %s", index,
+             strncmp(msg, "w8a16_gemm: ", 12) == 0 ? msg + 12 : msg);
+    return fail(status, buf);
+}
+
+int plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,
+                 w8a16_plan_t *out)
+{
+    char buf[256];
+    if (!descs || !out)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_gemm_batched: null descriptors or plan");
+    if (count < 1 || count > W8A16_MAX_BATCH) {
+        snprintf(buf, sizeof buf, "w8a16_gemm_batched: count=%u must be in 1..%u", count,
+                 (unsigned)W8A16_MAX_BATCH);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    uint32_t max_m = 0, min_ksteps = 0xffffffffu;
+    for (uint32_t i = 0; i < count; ++i) {
+        const w8a16_gemm_desc_t &d = descs[i];
+        int st = check_args(d.m, d.n, d.k, d.k, d.n);
+        if (st != W8A16_OK)
+            return fail_at(st, i);
+        if (d.m > 64) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_gemm_batched: descriptor %u: m=%u exceeds the batched tier's 64 rows",
+                     i, d.m);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        max_m = d.m > max_m ? d.m : max_m;
+        min_ksteps = d.k / kKStep < min_ksteps ? d.k / kKStep : min_ksteps;
+    }
+    // One stream-kernel variant for all problems, chosen as the single-GEMM
+    // rule chooses it for the tallest problem and the total column count:
+    // 16-row blocks covering m, the widest column tile that still gives
+    // about three quarters of the CUs a tile, waves by blocks per tile.
+    w8a16_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.cu_count = cu_count ? cu_count : kDefaultCUs;
+    p.kernel = W8A16_KERNEL_STREAM;
+    p.m_blocks = max_m <= 16 ? 1 : (max_m <= 32 ? 2 : 4);
+    p.depth = 1;
+    p.splits = 1;
+    const uint32_t fill = (3 * p.cu_count) / 4;
+    auto tiles_for = [&](uint32_t nbw) {
+        uint64_t t = 0;
+        for (uint32_t i = 0; i < count; ++i)
+            t += (uint64_t)div_up(descs[i].m, 16 * p.m_blocks) * div_up(descs[i].n, 16 * nbw);
+        return t;
+    };
+    p.n_blocks = 1;
+    const uint32_t cands[3] = {4, 2, 1};
+    for (uint32_t c : cands)
+        if (stream_shape_supported(p.m_blocks, c) && tiles_for(c) >= fill) {
+            p.n_blocks = c;
+            break;
+        }
+    const uint32_t pairs = p.m_blocks * p.n_blocks;
+    p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
+    while (p.waves > 4 && min_ksteps < 2 * p.waves)
+        p.waves /= 2;
+    // Finalize against the tallest, widest, longest problem for the block,
+    // LDS and variant checks; then describe the whole grid.
+    uint32_t max_n = 0, max_k = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+        max_n = descs[i].n > max_n ? descs[i].n : max_n;
+        max_k = descs[i].k > max_k ? descs[i].k : max_k;
+    }
+    int st = plan_finalize(max_m, max_n, max_k, &p);
+    if (st != W8A16_OK)
+        return st;
+    const uint64_t grid = tiles_for(p.n_blocks);
+    if (grid > 0x7fffffffull)
+        return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_batched: grid too large");
+    p.grid = (uint32_t)grid;
+    p.m_tiles = div_up(max_m, 16 * p.m_blocks);
+    p.n_tiles = 0;
+    for (uint32_t i = 0; i < count; ++i)
+        p.n_tiles += div_up(descs[i].n, 16 * p.n_blocks);
+    p.steps_per_split = max_k / kKStep;
+    *out = p;
+    return W8A16_OK;
+}
+
 }  // namespace w8a16
 
 extern "C" {
+
+int w8a16_plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,
+                       w8a16_plan_t *out)
+{
+    return w8a16::plan_batched(descs, count, cu_count, out);
+}
 
 int w8a16_check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
                      uint32_t c_row_stride)

@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -74,8 +76,10 @@ __device__ __forceinline__ f32x4_t sum_waves(const f32x4_t *red, uint32_t pi, ui
     return s;
 }
 
+// One workgroup's share of one GEMM: logical workgroup `lid` of g's grid
+// (split lid % splits of tile lid / splits).
 template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
+__device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -83,7 +87,6 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
     // The wave index is the same for all lanes of a wave; saying so lets the
     // per-step scale loads be scalar loads.
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
     const uint32_t split = lid % g.splits;
     const uint32_t tile = lid / g.splits;
     const uint32_t m_tile = tile % g.m_tiles;
@@ -313,9 +316,38 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
 }
 
 template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
-hipError_t launch_stream_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+__global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
 {
-    auto kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
+    stream_tile<MB, NBW, DEPTH, DIRECT, WAVES>(g, logical_wg(blockIdx.x, gridDim.x));
+}
+
+// Several independent GEMMs in one grid: problem i owns logical workgroups
+// start[i] .. start[i + 1] - 1 (no K splits).  The problem is picked with
+// wave-uniform selects, so its arguments stay in scalar registers.
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w8a16_stream_batched_kernel(BatchArgs b)
+{
+    const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
+    GemmArgs g = b.g[0];
+    uint32_t base = 0;
+#pragma unroll
+    for (uint32_t i = 1; i < W8A16_MAX_BATCH; ++i)
+        if (i < b.count && lid >= b.start[i]) {
+            g = b.g[i];
+            base = b.start[i];
+        }
+    stream_tile<MB, NBW, DEPTH, DIRECT, WAVES>(g, lid - base);
+}
+
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES, typename Args>
+hipError_t launch_stream_t(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    constexpr bool batched = std::is_same<Args, BatchArgs>::value;
+    void (*kern)(Args);
+    if constexpr (batched)
+        kern = w8a16_stream_batched_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
+    else
+        kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
     static bool attr_set = false;
     if (p.lds_bytes > 65536 && !attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -329,8 +361,8 @@ hipError_t launch_stream_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t
     return hipGetLastError();
 }
 
-template <int MB, int NBW, int DEPTH, bool DIRECT>
-hipError_t launch_stream_w(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+template <int MB, int NBW, int DEPTH, bool DIRECT, typename Args>
+hipError_t launch_stream_w(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     switch (p.block / 64) {
     case 4: return launch_stream_t<MB, NBW, DEPTH, DIRECT, 4>(g, p, stream);
@@ -340,24 +372,31 @@ hipError_t launch_stream_w(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t
     }
 }
 
-template <int MB, int NBW>
-hipError_t launch_stream_mn(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+// Batched launches are built for the default ring depth only (one K step
+// per wave in flight, staged A), which is what their planner chooses.
+template <int MB, int NBW, typename Args>
+hipError_t launch_stream_mn(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     const bool direct = (p.flags & W8A16_FLAG_DIRECT) != 0;
-    switch (p.depth * 2 + (direct ? 1 : 0)) {
-    case 2: return launch_stream_w<MB, NBW, 1, false>(g, p, stream);
-    case 3: return launch_stream_w<MB, NBW, 1, true>(g, p, stream);
-    case 4: return launch_stream_w<MB, NBW, 2, false>(g, p, stream);
-    case 5: return launch_stream_w<MB, NBW, 2, true>(g, p, stream);
-    case 8: return launch_stream_w<MB, NBW, 4, false>(g, p, stream);
-    case 9: return launch_stream_w<MB, NBW, 4, true>(g, p, stream);
-    default: return hipErrorInvalidValue;
+    if constexpr (std::is_same<Args, BatchArgs>::value) {
+        if (p.depth != 1 || direct)
+            return hipErrorInvalidValue;
+        return launch_stream_w<MB, NBW, 1, false>(g, p, stream);
+    } else {
+        switch (p.depth * 2 + (direct ? 1 : 0)) {
+        case 2: return launch_stream_w<MB, NBW, 1, false>(g, p, stream);
+        case 3: return launch_stream_w<MB, NBW, 1, true>(g, p, stream);
+        case 4: return launch_stream_w<MB, NBW, 2, false>(g, p, stream);
+        case 5: return launch_stream_w<MB, NBW, 2, true>(g, p, stream);
+        case 8: return launch_stream_w<MB, NBW, 4, false>(g, p, stream);
+        case 9: return launch_stream_w<MB, NBW, 4, true>(g, p, stream);
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
-}  // namespace
-
-hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+template <typename Args>
+hipError_t launch_stream_any(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     switch (p.m_blocks * 100 + p.n_blocks) {
     case 101: return launch_stream_mn<1, 1>(g, p, stream);
@@ -371,6 +410,18 @@ hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
     case 402: return launch_stream_mn<4, 2>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    return launch_stream_any(g, p, stream);
+}
+
+hipError_t launch_stream_batched(const BatchArgs &b, const w8a16_plan_t &p, hipStream_t stream)
+{
+    return launch_stream_any(b, p, stream);
 }
 
 }  // namespace w8a16

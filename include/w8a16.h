@@ -152,6 +152,45 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride,
                        uint32_t m, uint32_t n, uint32_t k,
                        const w8a16_plan_t *plan, void *stream);
 
+/* ---- Batched tier ------------------------------------------------------
+ * The pages' strided launch exists so that a multi-sequence Q/K/V tier can
+ * hold it as one arm among several with their own pitches (page
+ * "w8a16_gemm_pipelined_m32.rs", module doc and the doc comment of
+ * `w8a16_gemm_pipelined_m32_strided`).  Here the arms run in one launch. */
+
+/* Most GEMMs one batched call takes. */
+#define W8A16_MAX_BATCH 8
+
+/* One GEMM of a batch: the arguments of w8a16_gemm(), same meaning, layout
+ * and ownership (device pointers owned by the caller). */
+typedef struct w8a16_gemm_desc {
+    const void *a;            /* BF16 [m, a_row_stride] */
+    const void *w_fp8;        /* E4M3 [n, k] */
+    const float *block_scale; /* FP32 [ceil(n/128), k/128] */
+    void *c;                  /* BF16 [m, c_row_stride] */
+    uint32_t a_row_stride;
+    uint32_t c_row_stride;
+    uint32_t m, n, k;
+} w8a16_gemm_desc_t;
+
+/* Plan of a batched call from the descriptors' m, n and k (pointers and
+ * pitches are not read).  Pure: no GPU call.  One stream-kernel variant
+ * serves every problem, without K splits; grid is the total workgroup
+ * count, m_tiles the largest per problem and n_tiles the sum.  Errors:
+ * W8A16_ERR_NULL_PTR (descs or out null), W8A16_ERR_BAD_PLAN (count not in
+ * 1..W8A16_MAX_BATCH, or some m above 64), or the first failing problem's
+ * w8a16_check_args() code, with its index in w8a16_last_error(). */
+int w8a16_plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,
+                       w8a16_plan_t *out);
+
+/* `count` independent GEMMs (descs is a host array) in one launch of the
+ * stream kernel on `stream`; problem i computes exactly what w8a16_gemm()
+ * would with descs[i].  Each descriptor is checked as w8a16_gemm() checks
+ * its arguments, in order; on the first failure nothing is launched and
+ * that code is returned (index in w8a16_last_error()).  Asynchronous.  The
+ * problems' outputs must not overlap each other or any input. */
+int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream);
+
 /* Static text for a status code (never null). */
 const char *w8a16_status_string(int status);
 

@@ -260,3 +260,54 @@ def test_explicit_plans():
     with pytest.raises(w8.W8A16Error) as e:
         w8.make_plan(0, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 1)
     assert e.value.status == w8.ERR_M_ZERO
+
+
+# ------------------------------------------------------------ batched tier
+
+def test_batched_plan_one_variant_for_all_problems():
+    # decode-style Q/K/V arms: 8 rows, hidden 4096, grouped K/V heads
+    p = w8.plan_batched([(8, 4096, 4096), (8, 1024, 4096), (8, 1024, 4096)])
+    assert (p.kernel, p.m_blocks, p.splits, p.flags, p.depth) == (w8.KERNEL_STREAM, 1, 1, 0, 1)
+    nb = p.n_blocks
+    tiles = [-(-n // (16 * nb)) for n in (4096, 1024, 1024)]
+    assert p.grid == sum(tiles) and p.n_tiles == sum(tiles) and p.m_tiles == 1
+    assert p.grid >= 3 * 256 // 4          # fills about three quarters of the CUs
+    assert p.block == 64 * p.waves and p.lds_bytes <= 160 * 1024
+    # the tallest problem sets the row blocks; the shortest K the waves
+    p = w8.plan_batched([(40, 512, 1024), (3, 256, 256)])
+    assert p.m_blocks == 4 and p.m_tiles == 1
+    assert p.waves == 4                    # K = 256: two steps
+    assert w8.plan_batched([(17, 64, 128)]).m_blocks == 2
+
+
+def test_batched_rejections_name_the_descriptor():
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.plan_batched([])
+    assert e.value.status == w8.ERR_BAD_PLAN
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.plan_batched([(8, 64, 128)] * 9)
+    assert e.value.status == w8.ERR_BAD_PLAN
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.plan_batched([(8, 64, 128), (65, 64, 128)])
+    assert e.value.status == w8.ERR_BAD_PLAN and "descriptor 1" in str(e.value)
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.plan_batched([(8, 64, 128), (8, 64, 128), (8, 64, 100)])
+    assert e.value.status == w8.ERR_K_NOT_MULT_128
+    assert "descriptor 2: K=100" in str(e.value)
+
+
+def test_batched_gemm_rejects_before_any_gpu_call():
+    ok = dict(a=1 << 20, w_fp8=1 << 21, block_scale=1 << 22, c=1 << 23,
+              a_row_stride=128, c_row_stride=64, m=4, n=64, k=128)
+    assert w8.gemm_batched_raw([]) == w8.ERR_BAD_PLAN
+    bad = dict(ok, m=0)
+    assert w8.gemm_batched_raw([ok, bad]) == w8.ERR_M_ZERO
+    assert w8.last_error().startswith("w8a16_gemm_batched: descriptor 1: m=0")
+    bad = dict(ok, a_row_stride=100)
+    assert w8.gemm_batched_raw([bad, ok]) == w8.ERR_PITCH_TOO_SHORT
+    assert "descriptor 0" in w8.last_error()
+    bad = dict(ok, c=0)
+    assert w8.gemm_batched_raw([ok, ok, bad]) == w8.ERR_NULL_PTR
+    assert "descriptor 2" in w8.last_error()
+    bad = dict(ok, a_row_stride=132)
+    assert w8.gemm_batched_raw([ok, bad]) == w8.ERR_A_STRIDE_ALIGN

@@ -359,3 +359,91 @@ def test_argument_errors_with_device_pointers(w8):
                        64, 4, 64, 256) == w8.ERR_A_STRIDE_ALIGN
     torch.cuda.synchronize()
     assert torch.equal(before, c)
+
+
+# ------------------------------------------------------------ batched tier
+
+def run_gpu_batched(w8, probs, stream=None):
+    """Run every problem in one w8a16_gemm_batched call; returns each whole C
+    buffer (BF16 bits, pads and extra rows included)."""
+    keep, descs = [], []
+    for p in probs:
+        a, w, s, c = dev_u16(p.a), dev(p.w), dev(p.scale), dev_u16(p.c)
+        keep.append((a, w, s, c))
+        descs.append(dict(a=a.data_ptr(), w_fp8=w.data_ptr(), block_scale=s.data_ptr(),
+                          c=c.data_ptr(), a_row_stride=p.a_row_stride,
+                          c_row_stride=p.c_row_stride, m=p.m, n=p.n, k=p.k))
+    st = w8.gemm_batched_raw(descs, 0 if stream is None else stream.cuda_stream)
+    assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    return [t[3].cpu().numpy().view(np.uint16).reshape(p.c.shape) for t, p in zip(keep, probs)]
+
+
+BATCHES = [
+    # (m, n, k, a_row_stride, c_row_stride) per arm
+    [(8, 640, 1024, 1040, 700), (8, 128, 1024, 1024, 136), (8, 130, 1024, 1032, 130)],
+    [(1, 300, 256, 264, 301)],
+    [(24, 256, 384, None, None), (3, 520, 512, 520, 530), (17, 64, 128, None, 70),
+     (40, 200, 640, 648, 200)],
+    [(64, 96, 256, None, None)] * 8,
+]
+
+
+@pytest.mark.parametrize("arms", BATCHES)
+def test_batched_exact_data_bit_exact(w8, arms):
+    """Each arm of a batched call equals the oracle bit for bit on exact data
+    and leaves its pads and extra rows untouched."""
+    probs = [exact_problem(m, n, k, seed=50 + i, a_row_stride=ars, c_row_stride=crs,
+                           c_extra_rows=2)
+             for i, (m, n, k, ars, crs) in enumerate(arms)]
+    outs = run_gpu_batched(w8, probs)
+    for p, g in zip(probs, outs):
+        check_full(p, g, exact=True)
+
+
+def test_batched_equals_single_calls_with_the_same_variant(w8):
+    """The batched grid runs the single-GEMM kernel body: each arm is bitwise
+    the single call with the batched plan's variant (random data)."""
+    arms = [(16, 1000, 2048), (16, 256, 2048), (5, 384, 1024)]
+    probs = [datagen.make_problem(m, n, k, seed=90 + i, c_extra_rows=1)
+             for i, (m, n, k) in enumerate(arms)]
+    bp = w8.plan_batched(arms)
+    outs = run_gpu_batched(w8, probs)
+    for p, g in zip(probs, outs):
+        single = w8.make_plan(p.m, p.n, p.k, w8.KERNEL_STREAM, bp.m_blocks, bp.n_blocks, 1,
+                              bp.depth, 0, bp.waves)
+        assert np.array_equal(g, run_gpu(w8, p, single))
+        check_full(p, g)
+
+
+def test_batched_qkv_at_size_sampled(w8):
+    """Decode-size Q/K/V arms (8 rows, hidden 4096, K and V with 1024
+    columns), sampled parity."""
+    probs = [datagen.make_problem(8, n, 4096, seed=7 + n, c_extra_rows=1)
+             for n in (4096, 1024, 1024)]
+    outs = run_gpu_batched(w8, probs, stream=torch.cuda.Stream())
+    for p, g in zip(probs, outs):
+        rows, cols = datagen.sample_indices(p.m, p.n, 400, seed=3)
+        oc, _, bound = oracle.gemm_at(p.a, p.w, p.scale, p.m, p.n, p.k, rows, cols,
+                                      a_row_stride=p.a_row_stride)
+        assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+        assert (g[p.m:, :] == p.c[p.m:, :]).all()
+
+
+def test_batched_torch_wrapper(w8):
+    p1 = datagen.make_problem(4, 256, 512, seed=1)
+    p2 = datagen.make_problem(4, 128, 512, seed=2)
+    ts = []
+    for p in (p1, p2):
+        a = dev_u16(p.a).view(torch.bfloat16)[:, :p.k]
+        w = dev(p.w)
+        s = dev(p.scale)
+        c = torch.empty((p.m, p.n), dtype=torch.bfloat16, device="cuda")
+        ts.append((a, w, s, c))
+    outs = w8.gemm_batched(ts)
+    torch.cuda.synchronize()
+    for p, c in zip((p1, p2), outs):
+        g = c.view(torch.int16).cpu().numpy().view(np.uint16)
+        oc, _, bound = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k,
+                                   a_row_stride=p.a_row_stride)
+        assert oracle.within_tolerance(g, oc, bound).all()
