@@ -14,6 +14,10 @@ doc comment of ``w8a16_gemm_pipelined_m32_strided``, the one-scale-per-K-step
 rule in the doc comment of ``W8A16_M32_K_BLOCK`` and the fold points of the
 module doc's "Numerics" paragraph.
 
+It also holds the FP8 activation quantizer and the W8A8 GEMM it feeds
+(page "fp8_act_quant.rs": per-token groups of 128 K elements), with the
+arithmetic reading stated at their functions.
+
 This module is argument marshalling around that C code, plus the parity
 tolerance the GPU result is graded with.
 
@@ -80,6 +84,17 @@ def _load():
                                              u32, u32p, u32p, ctypes.c_int64,
                                              u16p, f64p, f64p, ctypes.c_int]
         lib.oracle_w8a16_gemm_at.restype = ctypes.c_int
+        lib.oracle_e4m3_rne.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_rne.restype = ctypes.c_uint8
+        lib.oracle_act_quant.argtypes = [u16p, u32, u32, u32, u8p, u32, f32p]
+        lib.oracle_act_quant.restype = ctypes.c_int
+        lib.oracle_w8a8_gemm.argtypes = [u8p, u32, f32p, u8p, f32p, u16p, u32, u32, u32,
+                                         u32, f64p, f64p, ctypes.c_int]
+        lib.oracle_w8a8_gemm.restype = ctypes.c_int
+        lib.oracle_w8a8_gemm_at.argtypes = [u8p, u32, f32p, u8p, f32p, u32, u32, u32,
+                                            u32p, u32p, ctypes.c_int64, u16p, f64p, f64p,
+                                            ctypes.c_int]
+        lib.oracle_w8a8_gemm_at.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -174,6 +189,98 @@ def gemm_at(a: np.ndarray, w: np.ndarray, scale: np.ndarray, m: int, n: int,
         _ptr(scale, ctypes.c_float), m, n, k, _ptr(rows, ctypes.c_uint32),
         _ptr(cols, ctypes.c_uint32), ns, _ptr(c, ctypes.c_uint16),
         _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double),
+        int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape or sample index")
+    return c, tot, bound
+
+
+# ---------------------------------------------------------------------------
+# FP8 activation quantizer and W8A8 GEMM (page "fp8_act_quant.rs": per-token
+# groups of 128 K elements).  The arithmetic is a reading (the page gives
+# only the grouping): s = amax / 448 and code = E4M3 RNE of x / s, both
+# divisions in binary32, saturated to +-448; an all-zero group has s = 0.
+# ---------------------------------------------------------------------------
+
+def e4m3_rne(x: float) -> int:
+    """OCP E4M3FN code nearest to the float32 ``x`` (ties to even,
+    saturating, sign of zero kept)."""
+    return int(_load().oracle_e4m3_rne(float(np.float32(x))))
+
+
+def act_quant(a: np.ndarray, m: int, k: int, a_row_stride: Optional[int] = None,
+              q_row_stride: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token, per-128-group FP8 quantization of BF16 bits ``a``
+    [m, a_row_stride].  Returns (codes uint8 [m, q_row_stride], scales
+    float32 [m, k/128]); code columns past k are zero."""
+    a_row_stride = k if a_row_stride is None else int(a_row_stride)
+    q_row_stride = k if q_row_stride is None else int(q_row_stride)
+    a = np.ascontiguousarray(a, dtype=np.uint16).reshape(-1)
+    assert a.size >= (m - 1) * a_row_stride + k
+    q = np.zeros((m, q_row_stride), dtype=np.uint8)
+    s = np.zeros((m, k // K_BLOCK), dtype=np.float32)
+    rc = _load().oracle_act_quant(_ptr(a, ctypes.c_uint16), a_row_stride, m, k,
+                                  _ptr(q, ctypes.c_uint8), q_row_stride,
+                                  _ptr(s, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape m=%d k=%d" % (m, k))
+    return q, s
+
+
+def _check_w8a8(qa, sa, w, sw, m, n, k, qa_row_stride):
+    assert qa.dtype == np.uint8 and w.dtype == np.uint8
+    assert sa.dtype == np.float32 and sw.dtype == np.float32
+    assert qa.size >= (m - 1) * qa_row_stride + k and w.size >= n * k
+    assert sa.size >= m * (k // K_BLOCK)
+    assert sw.size >= ((n + K_BLOCK - 1) // K_BLOCK) * (k // K_BLOCK)
+
+
+def gemm_w8a8(qa: np.ndarray, sa: np.ndarray, w: np.ndarray, sw: np.ndarray, m: int,
+              n: int, k: int, qa_row_stride: Optional[int] = None, threads: int = 0
+              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Whole W8A8 GEMM: codes ``qa`` [m, qa_row_stride] with scales ``sa``
+    [m, k/128], weight codes ``w`` [n, k] with block scales ``sw``.  Returns
+    (c_bits [m, n], tot [m, n], bound [m, n])."""
+    qa_row_stride = k if qa_row_stride is None else int(qa_row_stride)
+    qa = np.ascontiguousarray(qa, dtype=np.uint8).reshape(-1)
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    sa = np.ascontiguousarray(sa, dtype=np.float32).reshape(-1)
+    sw = np.ascontiguousarray(sw, dtype=np.float32).reshape(-1)
+    _check_w8a8(qa, sa, w, sw, m, n, k, qa_row_stride)
+    c = np.zeros((m, n), dtype=np.uint16)
+    tot = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = _load().oracle_w8a8_gemm(
+        _ptr(qa, ctypes.c_uint8), qa_row_stride, _ptr(sa, ctypes.c_float),
+        _ptr(w, ctypes.c_uint8), _ptr(sw, ctypes.c_float), _ptr(c, ctypes.c_uint16), n,
+        m, n, k, _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape m=%d n=%d k=%d" % (m, n, k))
+    return c, tot, bound
+
+
+def gemm_w8a8_at(qa: np.ndarray, sa: np.ndarray, w: np.ndarray, sw: np.ndarray, m: int,
+                 n: int, k: int, rows: np.ndarray, cols: np.ndarray,
+                 qa_row_stride: Optional[int] = None, threads: int = 0
+                 ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Selected W8A8 outputs C[rows[s], cols[s]]: (c_bits, tot, bound)."""
+    qa_row_stride = k if qa_row_stride is None else int(qa_row_stride)
+    qa = np.ascontiguousarray(qa, dtype=np.uint8).reshape(-1)
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    sa = np.ascontiguousarray(sa, dtype=np.float32).reshape(-1)
+    sw = np.ascontiguousarray(sw, dtype=np.float32).reshape(-1)
+    _check_w8a8(qa, sa, w, sw, m, n, k, qa_row_stride)
+    rows = np.ascontiguousarray(rows, dtype=np.uint32).reshape(-1)
+    cols = np.ascontiguousarray(cols, dtype=np.uint32).reshape(-1)
+    ns = rows.size
+    c = np.empty(ns, dtype=np.uint16)
+    tot = np.empty(ns, dtype=np.float64)
+    bound = np.empty(ns, dtype=np.float64)
+    rc = _load().oracle_w8a8_gemm_at(
+        _ptr(qa, ctypes.c_uint8), qa_row_stride, _ptr(sa, ctypes.c_float),
+        _ptr(w, ctypes.c_uint8), _ptr(sw, ctypes.c_float), m, n, k,
+        _ptr(rows, ctypes.c_uint32), _ptr(cols, ctypes.c_uint32), ns,
+        _ptr(c, ctypes.c_uint16), _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double),
         int(threads))
     if rc != 0:
         raise ValueError("oracle: invalid shape or sample index")

@@ -32,6 +32,9 @@
  * total before rounding and the bound B[i][j] = sum |A*W| * |S| that the
  * parity tolerance is written in.
  *
+ * The second part of the file (after the W8A16 GEMM) is the FP8 activation
+ * quantizer and the W8A8 GEMM; its readings are stated there.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math).
  */
 #include <math.h>
@@ -235,4 +238,193 @@ int oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------------
+ * FP8 activation quantizer and W8A8 GEMM (page "fp8_act_quant.rs": one
+ * quantization group is 128 K elements of one token; the page gives the
+ * grouping, not the arithmetic).  Reading taken for the arithmetic, the
+ * same rule as the weight blocks' scales: per (token, group)
+ *     s = amax / 448            (binary32 division, 448 = largest E4M3FN)
+ *     code_t = E4M3_RNE(clamp(x_t / s, -448, 448))   (binary32 division)
+ * and an all-zero group gets s = 0 and +0 codes.  Both divisions are single
+ * precision because the codes are integers decided by them: the kernel and
+ * the oracle must take that decision in the same precision.
+ * ------------------------------------------------------------------------ */
+
+/* OCP E4M3FN code nearest to x, ties to even, saturating to +-448 (NaN ->
+ * 0x7F).  Zero keeps its sign (-0 -> 0x80), and so does a value that rounds
+ * to zero.  Below 2^-6 the spacing is the subnormal 2^-9; in binade
+ * [2^e, 2^(e+1)) it is 2^(e-3).  a / spacing is exact in double. */
+uint8_t oracle_e4m3_rne(float x)
+{
+    double a, r;
+    int ex, e;
+    unsigned code;
+    const unsigned sign = signbit(x) ? 0x80u : 0u;
+
+    if (isnan(x))
+        return 0x7Fu;
+    a = fabs((double)x);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7Eu);
+    if (a < ldexp(1.0, -6)) {
+        r = nearbyint(a / ldexp(1.0, -9));      /* 0..8; 8 is the code of 2^-6 */
+        return (uint8_t)(sign | (unsigned)r);
+    }
+    frexp(a, &ex);
+    e = ex - 1;                                 /* floor(log2 a), -6..8 */
+    r = nearbyint(a / ldexp(1.0, e - 3));       /* 8..16 */
+    if (r == 16.0) {
+        r = 8.0;
+        e += 1;
+    }
+    code = ((unsigned)(e + 7) << 3) | ((unsigned)r - 8u);
+    if (code > 0x7Eu)
+        code = 0x7Eu;
+    return (uint8_t)(sign | code);
+}
+
+/* Quantize A (BF16 [m, a_row_stride], first k of each row) to codes
+ * q [m, q_row_stride] and scales [m, k/128] (row-major). */
+int oracle_act_quant(const uint16_t *a, uint32_t a_row_stride, uint32_t m, uint32_t k,
+                     uint8_t *q, uint32_t q_row_stride, float *scales)
+{
+    const uint32_t groups = k / ORACLE_K_BLOCK;
+
+    if (m == 0 || k == 0 || k % ORACLE_K_BLOCK != 0 || a_row_stride < k ||
+        q_row_stride < k)
+        return -1;
+    for (uint32_t i = 0; i < m; ++i) {
+        for (uint32_t g = 0; g < groups; ++g) {
+            const uint16_t *x = a + (size_t)i * a_row_stride + (size_t)g * ORACLE_K_BLOCK;
+            uint8_t *out = q + (size_t)i * q_row_stride + (size_t)g * ORACLE_K_BLOCK;
+            float amax = 0.0f, s;
+            for (uint32_t t = 0; t < ORACLE_K_BLOCK; ++t) {
+                float v = (float)oracle_bf16_value(x[t]);   /* exact */
+                if (fabsf(v) > amax)
+                    amax = fabsf(v);
+            }
+            s = amax / 448.0f;
+            scales[(size_t)i * groups + g] = s;
+            for (uint32_t t = 0; t < ORACLE_K_BLOCK; ++t) {
+                float y;
+                if (s == 0.0f) {
+                    out[t] = 0u;
+                    continue;
+                }
+                y = (float)oracle_bf16_value(x[t]) / s;
+                if (y > 448.0f)
+                    y = 448.0f;
+                if (y < -448.0f)
+                    y = -448.0f;
+                out[t] = oracle_e4m3_rne(y);
+            }
+        }
+    }
+    return 0;
+}
+
+/* One W8A8 output: blocks in ascending order, each block's exact partial
+ * dot product of decoded codes times the product of its two scales (A's for
+ * the row and K step, W's for the 128x128 weight block), in double. */
+static void oracle_w8a8_element(const uint8_t *qa, uint32_t qa_row_stride,
+                                const float *sa, const uint8_t *w, const float *sw,
+                                uint32_t i, uint32_t j, uint32_t k,
+                                const double table[256], double *tot_out,
+                                double *bound_out)
+{
+    const uint32_t kb = k / ORACLE_K_BLOCK;
+    const uint8_t *arow = qa + (size_t)i * qa_row_stride;
+    const uint8_t *wrow = w + (size_t)j * k;
+    const float *swrow = sw + (size_t)(j / ORACLE_K_BLOCK) * kb;
+    const float *sarow = sa + (size_t)i * kb;
+    double tot = 0.0, bound = 0.0;
+
+    for (uint32_t b = 0; b < kb; ++b) {
+        double p = 0.0, pabs = 0.0;
+        for (uint32_t t = 0; t < ORACLE_K_BLOCK; ++t) {
+            uint32_t kk = b * ORACLE_K_BLOCK + t;
+            double prod = table[arow[kk]] * table[wrow[kk]];
+            p += prod;
+            pabs += fabs(prod);
+        }
+        double s = (double)sarow[b] * (double)swrow[b];
+        tot += s * p;
+        bound += fabs(s) * pabs;
+    }
+    *tot_out = tot;
+    if (bound_out)
+        *bound_out = bound;
+}
+
+/* Full W8A8 GEMM: qa E4M3 [m, qa_row_stride], sa FP32 [m, k/128], w E4M3
+ * [n, k], sw FP32 [ceil(n/128), k/128]; outputs as oracle_w8a16_gemm. */
+int oracle_w8a8_gemm(const uint8_t *qa, uint32_t qa_row_stride, const float *sa,
+                     const uint8_t *w, const float *sw, uint16_t *c, uint32_t c_row_stride,
+                     uint32_t m, uint32_t n, uint32_t k, double *tot, double *bound,
+                     int nthreads)
+{
+    double table[256];
+    int64_t total, idx;
+
+    if (m == 0 || n == 0 || k == 0 || k % ORACLE_K_BLOCK != 0 ||
+        qa_row_stride < k || (c && c_row_stride < n))
+        return -1;
+    oracle_e4m3_table(table);
+    total = (int64_t)m * n;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (idx = 0; idx < total; ++idx) {
+        uint32_t i = (uint32_t)(idx / n), j = (uint32_t)(idx % n);
+        double t, bnd;
+        oracle_w8a8_element(qa, qa_row_stride, sa, w, sw, i, j, k, table, &t, &bnd);
+        if (c)
+            c[(size_t)i * c_row_stride + j] = oracle_bf16_rne(t);
+        if (tot)
+            tot[idx] = t;
+        if (bound)
+            bound[idx] = bnd;
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* Selected W8A8 outputs C[rows[s]][cols[s]]. */
+int oracle_w8a8_gemm_at(const uint8_t *qa, uint32_t qa_row_stride, const float *sa,
+                        const uint8_t *w, const float *sw, uint32_t m, uint32_t n,
+                        uint32_t k, const uint32_t *rows, const uint32_t *cols,
+                        int64_t nsamp, uint16_t *c_out, double *tot, double *bound,
+                        int nthreads)
+{
+    double table[256];
+    int64_t s;
+
+    if (m == 0 || n == 0 || k == 0 || k % ORACLE_K_BLOCK != 0 || qa_row_stride < k)
+        return -1;
+    for (s = 0; s < nsamp; ++s)
+        if (rows[s] >= m || cols[s] >= n)
+            return -1;
+    oracle_e4m3_table(table);
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (s = 0; s < nsamp; ++s) {
+        double t, bnd;
+        oracle_w8a8_element(qa, qa_row_stride, sa, w, sw, rows[s], cols[s], k, table, &t,
+                            &bnd);
+        if (c_out)
+            c_out[s] = oracle_bf16_rne(t);
+        if (tot)
+            tot[s] = t;
+        if (bound)
+            bound[s] = bnd;
+    }
+    (void)nthreads;
+    return 0;
 }

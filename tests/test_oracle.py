@@ -352,3 +352,196 @@ def test_golden_regression_small_workload():
     p = datagen.make_workload(datagen.workload("m1_n256_k256"))
     c, _, _ = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k)
     assert np.array_equal(c.reshape(-1), want.reshape(-1))
+
+
+# ----------------------------------------------- FP8 activation quantizer
+
+def _e4m3_positive_values():
+    """(value, code) of every finite non-negative E4M3FN code, ascending,
+    decoded by torch (independent of the oracle)."""
+    codes = list(range(0, 0x7F))
+    return list(zip(torch_e4m3(codes), codes))
+
+
+def brute_e4m3_rne(x: float) -> int:
+    """Nearest E4M3FN code to x by search over all finite values, ties to the
+    even code, saturating at 448, sign kept (also for zero)."""
+    sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+    a = Fraction(abs(float(x)))
+    best = None
+    for v, c in _e4m3_positive_values():
+        d = abs(Fraction(v) - a)
+        key = (d, c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return sign | best[1]
+
+
+def test_e4m3_rne_round_trips_every_finite_code():
+    for c in FINITE_CODES:
+        v = oracle.e4m3_value(c)
+        assert oracle.e4m3_rne(v) == c, hex(c)
+
+
+def test_e4m3_rne_ties_go_to_the_even_code():
+    vals = _e4m3_positive_values()
+    for (v0, c0), (v1, c1) in zip(vals, vals[1:]):
+        mid = (v0 + v1) / 2                       # exact in binary32
+        want = c0 if c0 % 2 == 0 else c1
+        assert oracle.e4m3_rne(mid) == want, (v0, v1)
+        assert oracle.e4m3_rne(-mid) == 0x80 | want
+
+
+def test_e4m3_rne_matches_brute_force_and_torch():
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([
+        rng.uniform(-448, 448, 3000),
+        np.exp2(rng.uniform(-12, 9, 3000)) * rng.choice([-1.0, 1.0], 3000),
+    ]).astype(np.float32)
+    xs = np.clip(xs, -448, 448)
+    t = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for x, tc in zip(xs[:800], t[:800]):
+        assert oracle.e4m3_rne(x) == brute_e4m3_rne(float(x)), float(x)
+    got = np.array([oracle.e4m3_rne(x) for x in xs], dtype=np.uint8)
+    assert np.array_equal(got, t)
+
+
+def test_e4m3_rne_saturates_and_flushes():
+    assert oracle.e4m3_rne(448.0) == 0x7E
+    assert oracle.e4m3_rne(463.9) == 0x7E
+    assert oracle.e4m3_rne(1e30) == 0x7E and oracle.e4m3_rne(-1e30) == 0xFE
+    assert oracle.e4m3_rne(2.0 ** -10) == 0x00           # tie at half the least subnormal
+    assert oracle.e4m3_rne(2.0 ** -10 * 1.0001) == 0x01
+    assert oracle.e4m3_rne(-(2.0 ** -11)) == 0x80        # rounds to zero, keeps the sign
+    assert oracle.e4m3_rne(-0.0) == 0x80 and oracle.e4m3_rne(0.0) == 0x00
+
+
+def _act(m, k, seed, pitch=None):
+    rng = np.random.default_rng(seed)
+    pitch = k if pitch is None else pitch
+    a = np.full((m, pitch), datagen.A_PAD_BITS, dtype=np.uint16)
+    a[:, :k] = torch_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    return a
+
+
+def test_act_quant_codes_are_torch_e4m3_of_x_over_s():
+    """Each code is the E4M3 cast (torch) of x / s in binary32, the group
+    maximum lands on +-448, and s is the largest |x| over 448."""
+    m, k = 3, 512
+    a = _act(m, k, 1, pitch=520)
+    q, s = oracle.act_quant(a, m, k, a_row_stride=520, q_row_stride=528)
+    x = (a[:, :k].astype(np.uint32) << 16).view(np.float32)
+    for i in range(m):
+        for g in range(k // 128):
+            xs = x[i, 128 * g:128 * g + 128]
+            assert s[i, g] > 0
+            y = np.clip(xs / s[i, g], -448, 448).astype(np.float32)
+            want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(q[i, 128 * g:128 * g + 128], want)
+            j = int(np.argmax(np.abs(xs)))
+            assert q[i, 128 * g + j] in (0x7E, 0xFE)
+            assert abs(float(s[i, g]) * 448 - float(np.abs(xs).max())) <= \
+                float(np.abs(xs).max()) * 2.0 ** -23
+    assert (q[:, k:] == 0).all()
+
+
+def test_act_quant_dequantization_error_bound():
+    """|e4m3(q) * s - x| <= 2^-4 |x| (normal range) + 2^-10 s (subnormal
+    half-spacing): three fraction bits, round to nearest."""
+    m, k = 4, 1024
+    a = _act(m, k, 2)
+    a[1, :128] = torch_bf16_bits(np.float32(np.linspace(-1e-3, 1e-3, 128)))  # small group
+    q, s = oracle.act_quant(a, m, k)
+    x = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dec = np.array(torch_e4m3(q.reshape(-1).tolist())).reshape(m, k)
+    srep = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(dec * srep - x)
+    assert (err <= np.abs(x) * 2.0 ** -4 + srep * 2.0 ** -10 + 1e-300).all()
+
+
+def test_act_quant_zero_group_and_power_of_two_scaling():
+    m, k = 2, 384
+    a = _act(m, k, 3)
+    a[0, 128:256] = 0
+    a[1, 256:384] = 0x8000                       # -0.0
+    q, s = oracle.act_quant(a, m, k)
+    assert s[0, 1] == 0 and (q[0, 128:256] == 0).all()
+    assert s[1, 2] == 0 and (q[1, 256:384] == 0).all()
+    # scaling a group by 2^e scales s by 2^e and keeps every code
+    x = (a.astype(np.uint32) << 16).view(np.float32)
+    a4 = torch_bf16_bits(x * np.float32(4.0))
+    q4, s4 = oracle.act_quant(a4, m, k)
+    assert np.array_equal(q4, q) and np.array_equal(s4, s * np.float32(4.0))
+
+
+# --------------------------------------------------------------- W8A8 GEMM
+
+def _exact_w8a8(qa, sa, w, sw, m, n, k):
+    av = np.array(torch_e4m3(qa.reshape(-1).tolist())).reshape(m, k)
+    wv = np.array(torch_e4m3(w.reshape(-1).tolist())).reshape(n, k)
+    out = []
+    for i in range(m):
+        row = []
+        for j in range(n):
+            tot = Fraction(0)
+            for b in range(k // 128):
+                p = sum(Fraction(av[i, kk]) * Fraction(wv[j, kk])
+                        for kk in range(128 * b, 128 * b + 128))
+                tot += Fraction(float(sa[i, b])) * Fraction(float(sw[j // 128, b])) * p
+            row.append(tot)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (2, 5, 256), (3, 130, 128)])
+def test_w8a8_equals_exact_rational_then_rne(m, n, k):
+    rng = np.random.default_rng(m * 7 + n + k)
+    qa = _rand_codes(rng, (m, k))
+    w = _rand_codes(rng, (n, k))
+    sa = np.exp2(rng.uniform(-10, 3, size=(m, k // 128))).astype(np.float32)
+    sw = np.exp2(rng.uniform(-12, -4, size=((n + 127) // 128, k // 128))).astype(np.float32)
+    sa[0, 0] = np.float32(0.3)
+    c, tot, bound = oracle.gemm_w8a8(qa, sa, w, sw, m, n, k)
+    exact = _exact_w8a8(qa, sa, w, sw, m, n, k)
+    for i in range(m):
+        for j in range(n):
+            x = exact[i][j]
+            assert abs(Fraction(tot[i, j]) - x) <= Fraction(bound[i, j]) * Fraction(2) ** -48
+            assert brute_bf16_rne(x) == c[i, j] or \
+                abs(x - (Fraction(oracle.bf16_value(int(c[i, j]))) +
+                         Fraction(oracle.bf16_value(brute_bf16_rne(x)))) / 2) <= \
+                Fraction(bound[i, j]) * Fraction(2) ** -48
+
+
+def test_w8a8_with_unit_a_scales_is_the_w8a16_gemm_of_the_decoded_codes():
+    """Every E4M3 value is a BF16 value: with all A scales 1 the W8A8 GEMM
+    of codes qa equals the (separately pinned) W8A16 GEMM of their BF16
+    decodings, bit for bit."""
+    m, n, k = 3, 260, 512
+    rng = np.random.default_rng(9)
+    qa = _rand_codes(rng, (m, k))
+    w = _rand_codes(rng, (n, k))
+    sw = np.exp2(rng.uniform(-12, -4, size=((n + 127) // 128, k // 128))).astype(np.float32)
+    a_bits = torch_bf16_bits(np.array(torch_e4m3(qa.reshape(-1).tolist()),
+                                      dtype=np.float32)).reshape(m, k)
+    c8, tot8, b8 = oracle.gemm_w8a8(qa, np.ones((m, k // 128), np.float32), w, sw, m, n, k)
+    c16, tot16, b16 = oracle.gemm(a_bits, w, sw, m, n, k)
+    assert np.array_equal(c8, c16) and np.array_equal(tot8, tot16)
+    rows = np.array([0, 2, 1]); cols = np.array([0, 259, 128])
+    ca, ta, _ = oracle.gemm_w8a8_at(qa, np.ones((m, k // 128), np.float32), w, sw, m, n, k,
+                                    rows, cols)
+    assert np.array_equal(ca, c8[rows, cols])
+
+
+def test_w8a8_pipeline_close_to_w8a16():
+    """Quantize-then-W8A8 stays within the quantization error of the W8A16
+    result: |C8 - C16| <= 2^-4 * B (three fraction bits per activation)."""
+    m, n, k = 2, 128, 512
+    a = _act(m, k, 4)
+    rng = np.random.default_rng(4)
+    w = _rand_codes(rng, (n, k))
+    sw = np.full((1, k // 128), 2.0 ** -6, np.float32)
+    q, s = oracle.act_quant(a, m, k)
+    _, t8, _ = oracle.gemm_w8a8(q, s, w, sw, m, n, k)
+    _, t16, b16 = oracle.gemm(a, w, sw, m, n, k)
+    assert (np.abs(t8 - t16) <= b16 * 2.0 ** -4 + 1e-30).all()
