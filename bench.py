@@ -19,6 +19,7 @@ Prints one JSON line.  Usage:
     python bench.py --traffic-run          (workload for rocprofv3 --pmc runs)
     python bench.py --m-sweep N K          (default plan for m = 1..256, one line each)
     python bench.py --batched              (Q/K/V arms in one batched call vs three calls)
+    python bench.py --w8a8                 (FP8 activation quantizer + W8A8 GEMM)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 
@@ -427,7 +428,109 @@ def batched_bench(m: int = 8, k: int = 4096, steps: int = 100, warmup: int = 10)
         "kernel_source_hash": kernel_source_hash(), "note": NOTE}), flush=True)
 
 
+W8A8_WORKLOADS = ["m8_n4096_k4096", "m16_n12288_k5120", "m32_n6144_k2048_strided"]
+
+
+def w8a8_bench(steps: int = 100, warmup: int = 10):
+    """The FP8-activation path on the workloads' shapes (contiguous pitches):
+    the quantizer alone, the W8A8 GEMM alone and both back to back, each
+    cold (replicas over >= 512 MiB) in graph replay.  One JSON line per
+    workload."""
+    import numpy as np
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    w8.library()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for name in W8A8_WORKLOADS:
+        wl = datagen.workload(name)
+        m, n, k = wl.m, wl.n, wl.k
+        p = datagen.make_problem(m, n, k, seed=wl.seed)
+        per = 2 * m * k + m * k + 4 * m * (k // 128) + p.w.nbytes + p.scale.nbytes + 2 * m * n
+        reps = max(1, -(-ARENA_BYTES // per))
+        dev = torch.device("cuda")
+        a = torch.from_numpy(p.a[:, :k].copy()).view(torch.int16).to(dev).reshape(1, -1).repeat(reps, 1)
+        q = torch.zeros((reps, m * k), dtype=torch.uint8, device=dev)
+        sa = torch.zeros((reps, m * (k // 128)), dtype=torch.float32, device=dev)
+        w = torch.from_numpy(p.w).to(dev).reshape(1, -1).repeat(reps, 1)
+        sw = torch.from_numpy(p.scale).to(dev).reshape(1, -1).repeat(reps, 1)
+        c = torch.zeros((reps, m * n), dtype=torch.int16, device=dev)
+        stream = torch.cuda.Stream()
+
+        def quant(i):
+            r = i % reps
+            st = w8.act_quant_fp8_raw(a[r].data_ptr(), k, q[r].data_ptr(), k, sa[r].data_ptr(),
+                                      m, k, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(w8.last_error())
+
+        def gemm(i):
+            r = i % reps
+            st = w8.gemm_w8a8_raw(q[r].data_ptr(), k, sa[r].data_ptr(), w[r].data_ptr(),
+                                  sw[r].data_ptr(), c[r].data_ptr(), n, m, n, k,
+                                  stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(w8.last_error())
+
+        def both(i):
+            quant(i)
+            gemm(i)
+
+        def graph_ms(fn):
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                for i in range(warmup):
+                    fn(i)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(steps):
+                        fn(warmup + i)
+                g.replay()
+                torch.cuda.synchronize()
+                start.record(stream)
+                g.replay()
+                stop.record(stream)
+                torch.cuda.synchronize()
+            return start.elapsed_time(stop) / steps
+
+        ms_both = graph_ms(both)
+        ms_q = graph_ms(quant)
+        ms_g = graph_ms(gemm)
+        ok = True
+        for r in range(min(reps, steps + warmup)):
+            cc = c[r].cpu().numpy().view(np.uint16)
+            ok &= bool(((cc & 0x7F80) != 0x7F80).all())
+        g_bytes = n * k + 4 * (-(-n // 128)) * (k // 128) + m * k + 4 * m * (k // 128) + 2 * m * n
+        q_bytes = 2 * m * k + m * k + 4 * m * (k // 128)
+        gbs = g_bytes / (ms_g * 1e-3) / 1e9
+        plan = w8.plan_w8a8(m, n, k, cus)
+        print(json.dumps({
+            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms_g, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+            "config": {"workload": "w8a8_" + name, "m": m, "n": n, "k": k, "weights": "cold",
+                       "arena_replicas": reps},
+            "us_per_call": round(ms_g * 1e3, 3),
+            "us_quantizer": round(ms_q * 1e3, 3),
+            "us_quantizer_plus_gemm": round(ms_both * 1e3, 3),
+            "quantizer_gbs": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "tflops": round(2.0 * m * n * k / (ms_g * 1e-3) / 1e12, 3),
+            "plan": plan.as_dict(), "output_sane": ok,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "w8a16_w8a8_kernel", "algorithmic_bytes_per_launch": g_bytes},
+            "kernel_source_hash": kernel_source_hash(), "note": NOTE}), flush=True)
+        del a, q, sa, w, sw, c
+        torch.cuda.empty_cache()
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--w8a8":
+        w8a8_bench()
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--batched":
         batched_bench()
         return

@@ -34,6 +34,7 @@ ERR_HIP = 8
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
 KERNEL_RING = 3
+KERNEL_W8A8 = 4
 
 FLAG_DIRECT = 1
 FLAG_A8 = 2
@@ -41,7 +42,8 @@ FLAG_A8 = 2
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
            "w8a16_gemm_planned", "w8a16_plan_batched", "w8a16_gemm_batched",
-           "w8a16_status_string", "w8a16_last_error")
+           "w8a16_act_quant_fp8", "w8a16_plan_w8a8", "w8a16_gemm_w8a8",
+           "w8a16_gemm_w8a8_planned", "w8a16_status_string", "w8a16_last_error")
 
 MAX_BATCH = 8
 
@@ -106,6 +108,15 @@ def library() -> ctypes.CDLL:
         lib.w8a16_plan_batched.restype = ctypes.c_int
         lib.w8a16_gemm_batched.argtypes = [ctypes.POINTER(GemmDesc), u32, vp]
         lib.w8a16_gemm_batched.restype = ctypes.c_int
+        lib.w8a16_act_quant_fp8.argtypes = [vp, u32, vp, u32, vp, u32, u32, vp]
+        lib.w8a16_act_quant_fp8.restype = ctypes.c_int
+        lib.w8a16_plan_w8a8.argtypes = [u32, u32, u32, u32, ctypes.POINTER(Plan)]
+        lib.w8a16_plan_w8a8.restype = ctypes.c_int
+        lib.w8a16_gemm_w8a8.argtypes = [vp, u32, vp, vp, vp, vp, u32, u32, u32, u32, vp]
+        lib.w8a16_gemm_w8a8.restype = ctypes.c_int
+        lib.w8a16_gemm_w8a8_planned.argtypes = [vp, u32, vp, vp, vp, vp, u32, u32, u32, u32,
+                                                ctypes.POINTER(Plan), vp]
+        lib.w8a16_gemm_w8a8_planned.restype = ctypes.c_int
         lib.w8a16_status_string.argtypes = [ctypes.c_int]
         lib.w8a16_status_string.restype = ctypes.c_char_p
         lib.w8a16_last_error.argtypes = []
@@ -260,3 +271,82 @@ def gemm_batched(problems, *, stream=None):
         stream = torch.cuda.current_stream(problems[0][0].device)
     _raise_if(gemm_batched_raw(descs, stream.cuda_stream))
     return [p[3] for p in problems]
+
+
+# ------------------------------------------------- FP8 activations, W8A8
+
+def plan_w8a8(m: int, n: int, k: int, cu_count: int = 0) -> Plan:
+    """Default plan of the W8A8 GEMM (no GPU call)."""
+    p = Plan()
+    _raise_if(library().w8a16_plan_w8a8(m, n, k, cu_count, ctypes.byref(p)))
+    return p
+
+
+def act_quant_fp8_raw(a_ptr: int, a_row_stride: int, q_ptr: int, q_row_stride: int,
+                      scales_ptr: int, m: int, k: int, stream: int = 0) -> int:
+    """Direct call of w8a16_act_quant_fp8; returns the status."""
+    return int(library().w8a16_act_quant_fp8(a_ptr, a_row_stride, q_ptr, q_row_stride,
+                                             scales_ptr, m, k, stream))
+
+
+def gemm_w8a8_raw(qa_ptr: int, qa_row_stride: int, a_scales_ptr: int, w_ptr: int,
+                  scale_ptr: int, c_ptr: int, c_row_stride: int, m: int, n: int, k: int,
+                  stream: int = 0, plan_: Optional[Plan] = None) -> int:
+    """Direct call of w8a16_gemm_w8a8 (or its planned form); returns the status."""
+    lib = library()
+    if plan_ is None:
+        return int(lib.w8a16_gemm_w8a8(qa_ptr, qa_row_stride, a_scales_ptr, w_ptr, scale_ptr,
+                                       c_ptr, c_row_stride, m, n, k, stream))
+    return int(lib.w8a16_gemm_w8a8_planned(qa_ptr, qa_row_stride, a_scales_ptr, w_ptr,
+                                           scale_ptr, c_ptr, c_row_stride, m, n, k,
+                                           ctypes.byref(plan_), stream))
+
+
+def act_quant_fp8(a, *, stream=None):
+    """Per-token, per-128-group FP8 quantization of a bfloat16 [m, k] CUDA
+    tensor (unit column stride, row stride a multiple of 8).  Returns
+    (codes uint8 [m, k], scales float32 [m, k/128])."""
+    import torch
+    if a.dim() != 2 or a.dtype != torch.bfloat16 or a.stride(1) != 1 or not a.is_cuda:
+        raise ValueError("a must be a 2-D bfloat16 CUDA tensor with unit column stride")
+    m, k = a.shape
+    q = torch.empty((m, k), dtype=torch.uint8, device=a.device)
+    s = torch.empty((m, max(0, k // 128)), dtype=torch.float32, device=a.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    a_rs = a.stride(0) if m > 1 else max(a.stride(0), k)
+    _raise_if(act_quant_fp8_raw(a.data_ptr(), a_rs, q.data_ptr(), k if k % 16 == 0 else k,
+                                s.data_ptr(), m, k, stream.cuda_stream))
+    return q, s
+
+
+def gemm_w8a8(qa, a_scales, w, scale, c=None, *, plan_: Optional[Plan] = None, stream=None):
+    """C = (FP8 activations qa [m, k] with scales [m, k/128]) @ dequant(W)^T
+    on the current (or given) torch stream.  Returns c (bfloat16 [m, n])."""
+    import torch
+    if qa.dim() != 2 or w.dim() != 2:
+        raise ValueError("qa and w must be 2-D")
+    m, k = qa.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("w must be [n, k] with the k of qa")
+    for t in (qa, w):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or t.stride(1) != 1:
+            raise ValueError("qa and w must be float8_e4m3fn or uint8 with unit column stride")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    for t in (a_scales, scale):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("scales must be contiguous float32")
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=qa.device)
+    if c.dtype != torch.bfloat16 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+        raise ValueError("c must be bfloat16 [m, n] with unit column stride")
+    if stream is None:
+        stream = torch.cuda.current_stream(qa.device)
+    q_rs = qa.stride(0) if m > 1 else max(qa.stride(0), k)
+    c_rs = c.stride(0) if m > 1 else max(c.stride(0), n)
+    _raise_if(gemm_w8a8_raw(qa.data_ptr(), q_rs, a_scales.data_ptr(), w.data_ptr(),
+                            scale.data_ptr(), c.data_ptr(), c_rs, m, n, k, stream.cuda_stream,
+                            plan_))
+    return c

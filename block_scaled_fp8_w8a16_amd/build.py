@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw8a16.so")
 
 SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_m64.hip", "tile_m128.hip",
-           "ring_kernel.hip"]
+           "ring_kernel.hip", "w8a8_kernel.hip"]
 HEADERS = ["plan.h", "kernels.h", "device_common.h", "tile_kernel.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,7 +32,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # first copies them out (v_accvgpr_read), which measured as the single most
 # expensive part of its loop.  The VGPR form of the MFMA keeps them in VGPRs.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"tile_m64.hip": _VGPR_FORM, "tile_m128.hip": _VGPR_FORM}
+EXTRA_FLAGS = {"tile_m64.hip": _VGPR_FORM, "tile_m128.hip": _VGPR_FORM,
+               "w8a8_kernel.hip": _VGPR_FORM}
 
 
 def _compile_cmd(src: str, obj: str) -> list:

@@ -202,8 +202,119 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
     st = plan_finalize(m, n, k, &p);
     if (st != W8A16_OK)
         return st;
+    if (p.kernel == W8A16_KERNEL_W8A8)
+        return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_planned: the W8A8 kernel takes FP8 "
+                                        "activations (w8a16_gemm_w8a8_planned)");
     return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, p,
                static_cast<hipStream_t>(stream));
+}
+
+int w8a16_act_quant_fp8(const void *a, uint32_t a_row_stride, void *q, uint32_t q_row_stride,
+                        float *scales, uint32_t m, uint32_t k, void *stream)
+{
+    using namespace w8a16;
+    // m, k, the A pitch and its alignment as w8a16_gemm checks them (n = 1
+    // stands for the absent output width), then the code pitch.
+    int st = check_args(m, 1, k, a_row_stride, 1);
+    if (st != W8A16_OK)
+        return fail_with_name(st, "w8a16_act_quant_fp8");
+    char buf[192];
+    if (q_row_stride < k) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_act_quant_fp8: q_row_stride=%u must cover k=%u", q_row_stride, k);
+        return fail(W8A16_ERR_PITCH_TOO_SHORT, buf);
+    }
+    if (q_row_stride % 16 != 0) {
+        snprintf(buf, sizeof buf,
+                 "w8a16_act_quant_fp8: q_row_stride=%u must keep rows 16B-aligned "
+                 "(multiple of 16)", q_row_stride);
+        return fail(W8A16_ERR_A_STRIDE_ALIGN, buf);
+    }
+    if (!a || !q || !scales)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_act_quant_fp8: a, q and scales must be non-null");
+    QuantArgs qa;
+    qa.a = static_cast<const uint8_t *>(a);
+    qa.q = static_cast<uint8_t *>(q);
+    qa.scales = scales;
+    qa.a_stride = a_row_stride;
+    qa.q_stride = q_row_stride;
+    qa.m = m;
+    qa.k = k;
+    hipError_t e = launch_act_quant(qa, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    set_last_error("");
+    return W8A16_OK;
+}
+
+int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float *a_scales,
+                            const void *w_fp8, const float *block_scale, void *c,
+                            uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
+                            const w8a16_plan_t *plan, void *stream)
+{
+    using namespace w8a16;
+    int st = check_call(qa, qa_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    if (st != W8A16_OK)
+        return st;
+    if (qa_row_stride % 16 != 0) {
+        char buf[160];
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm_w8a8: qa_row_stride=%u must keep FP8 rows 16B-aligned "
+                 "(multiple of 16)", qa_row_stride);
+        return fail(W8A16_ERR_A_STRIDE_ALIGN, buf);
+    }
+    if (!a_scales)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_gemm_w8a8: a_scales must be non-null");
+    w8a16_plan_t p;
+    if (plan) {
+        p = *plan;
+        st = plan_finalize(m, n, k, &p);
+        if (st != W8A16_OK)
+            return st;
+        if (p.kernel != W8A16_KERNEL_W8A8)
+            return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_w8a8: plan kernel must be "
+                                            "W8A16_KERNEL_W8A8");
+    } else {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetDevice");
+        uint32_t cus = 0;
+        st = device_cu_count(dev, &cus);
+        if (st != W8A16_OK)
+            return st;
+        st = make_plan_w8a8(m, n, k, cus, &p);
+        if (st != W8A16_OK)
+            return st;
+    }
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.a = static_cast<const uint8_t *>(qa);
+    g.w = static_cast<const uint8_t *>(w_fp8);
+    g.scale = block_scale;
+    g.c = static_cast<uint8_t *>(c);
+    g.a_stride = qa_row_stride;
+    g.c_stride = c_row_stride;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.m_tiles = p.m_tiles;
+    g.n_tiles = p.n_tiles;
+    g.splits = 1;
+    g.steps_per_split = k / kKStep;
+    hipError_t e = launch_w8a8(g, a_scales, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    set_last_error("");
+    return W8A16_OK;
+}
+
+int w8a16_gemm_w8a8(const void *qa, uint32_t qa_row_stride, const float *a_scales,
+                    const void *w_fp8, const float *block_scale, void *c,
+                    uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k, void *stream)
+{
+    return w8a16_gemm_w8a8_planned(qa, qa_row_stride, a_scales, w_fp8, block_scale, c,
+                                   c_row_stride, m, n, k, nullptr, stream);
 }
 
 int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream)

@@ -31,7 +31,20 @@ struct BatchArgs {
     uint32_t count;
 };
 
+// FP8 activation quantizer: A BF16 [m, a_stride] -> codes [m, q_stride] and
+// scales [m, k/128].
+struct QuantArgs {
+    const uint8_t *a;
+    uint8_t *q;
+    float *scales;
+    uint32_t a_stride, q_stride, m, k;
+};
+
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_act_quant(const QuantArgs &q, hipStream_t stream);
+// W8A8: g.a holds FP8 codes (g.a_stride in bytes), a_scales FP32 [m, k/128].
+hipError_t launch_w8a8(const GemmArgs &g, const float *a_scales, const w8a16_plan_t &p,
+                       hipStream_t stream);
 hipError_t launch_stream_batched(const BatchArgs &b, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m64(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m128(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);

@@ -80,6 +80,27 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
     }
 }
 
+static bool w8a8_shape_supported(uint32_t mb, uint32_t nb)
+{
+    switch (mb * 100 + nb) {
+    case 101: case 102: case 104:
+    case 201: case 202: case 204:
+    case 401: case 402:
+        return true;
+    default:
+        return false;
+    }
+}
+
+// W8A8 kernel LDS: per wave one K step of its weight and A blocks (16 rows x
+// 128 bytes each), reused for the wave-order reduction of the partial tiles.
+static uint32_t w8a8_lds_bytes(uint32_t mb, uint32_t nb, uint32_t waves)
+{
+    const uint32_t staging = waves * (nb + mb) * 2048u;
+    const uint32_t reduce = waves * nb * mb * kAccBytes;
+    return staging > reduce ? staging : reduce;
+}
+
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
 {
     return (mb == 4 || mb == 8) && (nb == 4 || nb == 8);
@@ -191,6 +212,28 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         p->stage_steps = 0;
         p->block = p->waves * 64;
         p->lds_bytes = tile_lds_bytes(p->m_blocks, p->n_blocks, p->depth, ast);
+        if (p->lds_bytes > kMaxLdsBytes) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
+                     p->lds_bytes, kMaxLdsBytes);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+    } else if (p->kernel == W8A16_KERNEL_W8A8) {
+        if (!w8a8_shape_supported(p->m_blocks, p->n_blocks) ||
+            (p->waves != 4 && p->waves != 8 && p->waves != 16) ||
+            (p->waves == 16 && p->m_blocks * p->n_blocks > 2) || p->flags != 0 ||
+            p->splits != 1) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: W8A8 kernel has no (m_blocks=%u, n_blocks=%u, waves=%u, "
+                     "flags=0x%x, splits=%u) variant", p->m_blocks, p->n_blocks, p->waves,
+                     p->flags, p->splits);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->depth = 2;
+        p->stage_steps = 0;
+        p->a_depth = 0;
+        p->block = p->waves * 64;
+        p->lds_bytes = w8a8_lds_bytes(p->m_blocks, p->n_blocks, p->waves);
         if (p->lds_bytes > kMaxLdsBytes) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",
@@ -381,6 +424,55 @@ const char *status_string(int status)
     }
 }
 
+int make_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    if (!out)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_plan: null plan");
+    int st = check_args(m, n, k, k, n);
+    if (st != W8A16_OK)
+        return st;
+    // The stream kernel's small-m rule: 16-row blocks covering up to 64
+    // rows (taller m takes several row tiles), the widest column tile that
+    // still gives about three quarters of the CUs a tile, waves by blocks
+    // per tile, at least two K steps per wave.  No K split.
+    w8a16_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.cu_count = cu_count ? cu_count : kDefaultCUs;
+    p.kernel = W8A16_KERNEL_W8A8;
+    p.m_blocks = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    p.splits = 1;
+    const uint32_t ksteps = k / kKStep;
+    const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
+    const uint32_t fill = (3 * p.cu_count) / 4;
+    p.n_blocks = 1;
+    const uint32_t cands[3] = {4, 2, 1};
+    for (uint32_t c : cands)
+        if (w8a8_shape_supported(p.m_blocks, c) && div_up(n, 16 * c) * m_tiles >= fill) {
+            p.n_blocks = c;
+            break;
+        }
+    const uint32_t pairs = p.m_blocks * p.n_blocks;
+    p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
+    while (p.waves > 4 && (ksteps < 2 * p.waves ||
+                           w8a8_lds_bytes(p.m_blocks, p.n_blocks, p.waves) > kMaxLdsBytes))
+        p.waves /= 2;
+    st = plan_finalize(m, n, k, &p);
+    if (st != W8A16_OK)
+        return st;
+    *out = p;
+    return W8A16_OK;
+}
+
+// Replace the "w8a16_gemm" prefix of the thread's last error by `name`.
+int fail_with_name(int status, const char *name)
+{
+    char buf[320];
+    const char *msg = last_error();
+    snprintf(buf, sizeof buf, "%s: %s", name,
+             strncmp(msg, "w8a16_gemm: ", 12) == 0 ? msg + 12 : msg);
+    return fail(status, buf);
+}
+
 // Prefix the thread's last error with the index of the descriptor it came
 // from and return `status`.
 int fail_at(int status, uint32_t index)
@@ -473,6 +565,11 @@ int plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_cou
 }  // namespace w8a16
 
 extern "C" {
+
+int w8a16_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    return w8a16::make_plan_w8a8(m, n, k, cu_count, out);
+}
 
 int w8a16_plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,
                        w8a16_plan_t *out)

@@ -121,8 +121,11 @@ int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
                uint32_t c_row_stride);
 int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);
 int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p);
+int make_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);
 int plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,
                  w8a16_plan_t *out);
+// Replace the "w8a16_gemm" prefix of the last error by `name`.
+int fail_with_name(int status, const char *name);
 // Prefix the last error with "w8a16_gemm_batched: descriptor <index>: ".
 int fail_at(int status, uint32_t index);
 const char *status_string(int status);

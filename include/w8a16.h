@@ -76,7 +76,11 @@ typedef enum w8a16_kernel {
      * stage_steps steps with a ring of `depth` stages in flight (1 KiB
      * row-contiguous LDS-DMA loads), and its waves, grouped per column
      * block, take the stages' steps round-robin.  No K split. */
-    W8A16_KERNEL_RING = 3
+    W8A16_KERNEL_RING = 3,
+    /* W8A8 kernel (w8a16_gemm_w8a8 only): A given as FP8 codes with one
+     * scale per (row, K step); the stream kernel's organisation with A
+     * staged like the weight and one FP8 MFMA per K step.  No K split. */
+    W8A16_KERNEL_W8A8 = 4
 } w8a16_kernel;
 
 /* Launch plan.  w8a16_plan() fills every field; callers may change
@@ -190,6 +194,48 @@ int w8a16_plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t 
  * that code is returned (index in w8a16_last_error()).  Asynchronous.  The
  * problems' outputs must not overlap each other or any input. */
 int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream);
+
+/* ---- FP8 activations and the W8A8 GEMM ----------------------------------
+ * The per-token FP8 activation quantizer of page "fp8_act_quant.rs" (one
+ * group = 128 consecutive K elements of one token; tokens on grid X, groups
+ * on grid Y) and the block-scaled GEMM that consumes its output.  The page
+ * gives the grouping, not the arithmetic; the reading used: per (token,
+ * group) s = amax / 448 and code = E4M3 round-to-nearest-even of x / s, both
+ * divisions in binary32, saturated to +-448; an all-zero group gets s = 0
+ * and zero codes. */
+
+/* Quantize a: BF16 [m, a_row_stride] (first k of each row) into q: E4M3
+ * [m, q_row_stride] (first k of each row written) and scales: FP32
+ * [m, k/128] row-major.  Device pointers owned by the caller.  Errors, in
+ * order: m == 0; k not a positive multiple of 128; a_row_stride or
+ * q_row_stride below k (W8A16_ERR_PITCH_TOO_SHORT); a_row_stride not a
+ * multiple of 8 or q_row_stride not a multiple of 16 (16-byte rows,
+ * W8A16_ERR_A_STRIDE_ALIGN); a null pointer.  Nothing is launched on an
+ * error.  Asynchronous on `stream`. */
+int w8a16_act_quant_fp8(const void *a, uint32_t a_row_stride, void *q, uint32_t q_row_stride,
+                        float *scales, uint32_t m, uint32_t k, void *stream);
+
+/* Default plan of the W8A8 GEMM (kernel W8A16_KERNEL_W8A8).  Pure. */
+int w8a16_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count,
+                    w8a16_plan_t *out);
+
+/*   C[i, j] = bf16( sum_b a_scales[i, b] * block_scale[j/128, b] *
+ *                   sum_t qa[i, 128b + t] * w_fp8[j, 128b + t] )
+ * qa: E4M3 [m, qa_row_stride]; a_scales: FP32 [m, k/128]; w_fp8 and
+ * block_scale as for w8a16_gemm; c: BF16 [m, c_row_stride].  The two scales
+ * are multiplied in FP32 and folded once per K step.  Checks as w8a16_gemm
+ * with qa_row_stride in place of a_row_stride, which must be a multiple of
+ * 16 (16-byte rows).  Asynchronous. */
+int w8a16_gemm_w8a8(const void *qa, uint32_t qa_row_stride, const float *a_scales,
+                    const void *w_fp8, const float *block_scale, void *c,
+                    uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* w8a16_gemm_w8a8 with an explicit plan (kernel must be W8A16_KERNEL_W8A8;
+ * m_blocks, n_blocks and waves taken from it).  For tests and tuning. */
+int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float *a_scales,
+                            const void *w_fp8, const float *block_scale, void *c,
+                            uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
+                            const w8a16_plan_t *plan, void *stream);
 
 /* Static text for a status code (never null). */
 const char *w8a16_status_string(int status);

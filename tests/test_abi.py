@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "w8a16.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w8a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w8a16_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -311,3 +311,52 @@ def test_batched_gemm_rejects_before_any_gpu_call():
     assert "descriptor 2" in w8.last_error()
     bad = dict(ok, a_row_stride=132)
     assert w8.gemm_batched_raw([ok, bad]) == w8.ERR_A_STRIDE_ALIGN
+
+
+# ------------------------------------------------- FP8 activations, W8A8
+
+def test_act_quant_rejects_in_order_before_any_gpu_call():
+    f = w8.act_quant_fp8_raw
+    assert f(1, 128, 2, 128, 3, 0, 128) == w8.ERR_M_ZERO
+    assert "w8a16_act_quant_fp8: m=0" in w8.last_error()
+    assert f(1, 128, 2, 128, 3, 1, 100) == w8.ERR_K_NOT_MULT_128
+    assert f(1, 120, 2, 128, 3, 1, 128) == w8.ERR_PITCH_TOO_SHORT
+    assert f(1, 128, 2, 112, 3, 1, 128) == w8.ERR_PITCH_TOO_SHORT
+    assert f(1, 132, 2, 128, 3, 1, 128) == w8.ERR_A_STRIDE_ALIGN
+    assert f(1, 136, 2, 136, 3, 1, 128) == w8.ERR_A_STRIDE_ALIGN   # codes need 16-byte rows
+    assert "q_row_stride=136" in w8.last_error()
+    assert f(0, 128, 2, 128, 3, 1, 128) == w8.ERR_NULL_PTR
+    assert f(1, 128, 2, 128, 0, 1, 128) == w8.ERR_NULL_PTR
+
+
+def test_w8a8_rejects_before_any_gpu_call():
+    f = w8.gemm_w8a8_raw
+    assert f(1, 128, 2, 3, 4, 5, 16, 0, 16, 128) == w8.ERR_M_ZERO
+    assert f(1, 136, 2, 3, 4, 5, 16, 1, 16, 128) == w8.ERR_A_STRIDE_ALIGN
+    assert "qa_row_stride=136" in w8.last_error()
+    assert f(1, 128, 0, 3, 4, 5, 16, 1, 16, 128) == w8.ERR_NULL_PTR
+    p = w8.plan(4, 64, 256)
+    assert f(1, 256, 2, 3, 4, 5, 64, 4, 64, 256, plan_=p) == w8.ERR_BAD_PLAN
+    p8 = w8.plan_w8a8(4, 64, 256)
+    assert w8.gemm_raw(1, 256, 3, 4, 5, 64, 4, 64, 256, plan_=p8) == w8.ERR_BAD_PLAN
+    assert "W8A8" in w8.last_error()
+
+
+def test_w8a8_plans():
+    p = w8.plan_w8a8(8, 4096, 4096)
+    assert (p.kernel, p.splits, p.depth, p.m_blocks) == (w8.KERNEL_W8A8, 1, 2, 1)
+    assert p.grid == p.m_tiles * p.n_tiles >= 192
+    assert p.lds_bytes == max(p.waves * (p.n_blocks + p.m_blocks) * 2048,
+                              p.waves * p.n_blocks * p.m_blocks * 1024)
+    for m, n, k in [(1, 256, 256), (16, 12288, 5120), (32, 6144, 2048), (48, 1000, 384),
+                    (200, 300, 1024)]:
+        p = w8.plan_w8a8(m, n, k)
+        _covers(p, m, n, k)
+        assert p.waves * 2 <= max(8, k // 128) or p.waves == 4
+        assert p.waves != 16 or p.m_blocks * p.n_blocks <= 2
+    with pytest.raises(w8.W8A16Error):          # 16 waves only with <= 2 blocks
+        w8.make_plan(32, 256, 4096, w8.KERNEL_W8A8, 2, 2, 1, waves=16)
+    with pytest.raises(w8.W8A16Error):          # no K split
+        w8.make_plan(32, 256, 4096, w8.KERNEL_W8A8, 2, 2, 2, waves=8)
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(32, 256, 4096, w8.KERNEL_W8A8, 4, 4, 1, waves=8)

@@ -447,3 +447,148 @@ def test_batched_torch_wrapper(w8):
         oc, _, bound = oracle.gemm(p.a, p.w, p.scale, p.m, p.n, p.k,
                                    a_row_stride=p.a_row_stride)
         assert oracle.within_tolerance(g, oc, bound).all()
+
+
+# ------------------------------------------------- FP8 activations, W8A8
+
+def run_act_quant(w8, a_bits, m, k, a_row_stride, q_row_stride):
+    a = dev_u16(a_bits)
+    q = torch.full((m, q_row_stride), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((m, k // 128), -1.0, dtype=torch.float32, device="cuda")
+    st = w8.act_quant_fp8_raw(a.data_ptr(), a_row_stride, q.data_ptr(), q_row_stride,
+                              s.data_ptr(), m, k)
+    assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,k,a_pad,q_pad", [(1, 128, 0, 0), (5, 384, 8, 16), (33, 4096, 0, 0),
+                                             (300, 1024, 24, 32), (2, 128 * 200, 0, 0)])
+def test_act_quant_bit_exact(w8, m, k, a_pad, q_pad):
+    """Codes and scales equal the oracle's bit for bit (both divide in
+    binary32); code pads are untouched."""
+    p = datagen.make_problem(m, 1, k, seed=m + k, a_row_stride=k + a_pad)
+    if m >= 3:
+        p.a[1, :128] = 0                          # zero group
+        p.a[2, 128 * (k // 256):128 * (k // 256) + 128] = 0x8000   # -0 group
+        tiny = np.float32(np.linspace(-1e-30, 1e-30, 128))
+        p.a[0, :128] = datagen.to_bf16_bits(tiny)
+    q, s = run_act_quant(w8, p.a, m, k, k + a_pad, k + q_pad)
+    oq, os_ = oracle.act_quant(p.a, m, k, a_row_stride=k + a_pad, q_row_stride=k + q_pad)
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    bad = np.argwhere(q[:, :k] != oq[:, :k])
+    assert bad.size == 0, (bad[:5].tolist(), q[tuple(bad[:5].T)], oq[tuple(bad[:5].T)])
+    assert (q[:, k:] == 0xAB).all()
+
+
+def test_act_quant_rounding_ties_and_subnormals(w8):
+    """With the group maximum 448 the scale is exactly 1 and the codes are
+    the E4M3 rounding of the inputs themselves: every midpoint between two
+    adjacent E4M3 values (ties to even), and values around the subnormal
+    range, against the oracle's encoder."""
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    mids = [(x + y) / 2 for x, y in zip(pos, pos[1:])]
+    extra = [2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 2.0 ** -9 * 7.5, 2.0 ** -6 * 0.96875]
+    vals = np.array([448.0] + mids + [-v for v in mids] + extra + [-v for v in extra],
+                    dtype=np.float32)
+    k = 128 * (-(-vals.size // 127))
+    rows = []
+    for g in range(k // 128):
+        chunk = vals[127 * g:127 * (g + 1)]
+        row = np.zeros(128, np.float32)
+        row[0] = 448.0
+        row[1:1 + chunk.size] = chunk
+        rows.append(row)
+    x = np.concatenate(rows)[None, :]
+    bits = datagen.to_bf16_bits(x)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), x)   # exact in BF16
+    q, s = run_act_quant(w8, bits, 1, k, k, k)
+    oq, os_ = oracle.act_quant(bits, 1, k)
+    assert (s == 1.0).all() and (os_ == 1.0).all()
+    assert np.array_equal(q[:, :k], oq)
+
+
+def exact_w8a8_problem(m, n, k, seed, qa_pad=0, c_row_stride=None):
+    """W8A8 operands whose products and FP32 sums are exact: activation
+    values in {0, +-1/8, ..., +-1}, weight codes below 0x38 (|w| < 1,
+    subnormals included), scales in {1, 2}, K <= 512."""
+    assert k <= 512
+    rng = np.random.default_rng(seed)
+    act_vals = np.array([j / 8.0 for j in range(-8, 9)], np.float32)
+    qa = np.zeros((m, k + qa_pad), np.uint8)
+    qa[:, :k] = np.vectorize(oracle.e4m3_rne)(rng.choice(act_vals, size=(m, k)))
+    mag = rng.integers(0, 0x38, size=(n, k), dtype=np.uint8)
+    w = mag | (rng.integers(0, 2, size=(n, k), dtype=np.uint8) << 7)
+    sa = rng.choice(np.float32([1.0, 2.0]), size=(m, k // 128))
+    sw = rng.choice(np.float32([1.0, 2.0]), size=((n + 127) // 128, k // 128))
+    return qa, sa, w, sw
+
+
+def run_w8a8(w8, qa, sa, w, sw, m, n, k, qa_row_stride, c_row_stride, c_rows, plan=None):
+    dq, dsa, dw, dsw = dev(qa), dev(sa), dev(w), dev(sw)
+    c = torch.full((c_rows, c_row_stride), 0x7777, dtype=torch.int16, device="cuda")
+    st = w8.gemm_w8a8_raw(dq.data_ptr(), qa_row_stride, dsa.data_ptr(), dw.data_ptr(),
+                          dsw.data_ptr(), c.data_ptr(), c_row_stride, m, n, k, 0, plan)
+    assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    return c.cpu().numpy().view(np.uint16)
+
+
+W8A8_VARIANTS = [(1, 1, 4), (1, 1, 8), (1, 1, 16), (1, 2, 8), (1, 2, 16), (1, 4, 4),
+                 (1, 4, 8), (2, 1, 8), (2, 1, 16), (2, 2, 8), (2, 4, 4), (2, 4, 8),
+                 (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 2, 8)]
+
+
+@pytest.mark.parametrize("mb,nb,waves", W8A8_VARIANTS)
+@pytest.mark.parametrize("m", [3, 40])
+def test_w8a8_exact_data_every_variant(w8, mb, nb, waves, m):
+    n, k = 16 * nb * 2 + 5, 384
+    qa, sa, w, sw = exact_w8a8_problem(m, n, k, seed=mb * 100 + nb * 10 + waves + m, qa_pad=16)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_W8A8, mb, nb, 1, waves=waves)
+    c = run_w8a8(w8, qa, sa, w, sw, m, n, k, k + 16, n + 3, m + 1, plan)
+    oc, _, _ = oracle.gemm_w8a8(qa, sa, w, sw, m, n, k, qa_row_stride=k + 16)
+    bad = np.argwhere(c[:m, :n] != oc)
+    assert bad.size == 0, (bad[:5].tolist(), c[tuple(bad[:5].T)], oc[tuple(bad[:5].T)])
+    assert (c[:m, n:] == 0x7777).all() and (c[m:, :] == 0x7777).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 256), (8, 4096, 4096), (16, 12288, 5120),
+                                   (32, 6144, 2048), (100, 700, 1280)])
+def test_w8a8_default_plan_within_tolerance(w8, m, n, k):
+    """Random codes and log-uniform scales, default plan, sampled against
+    the oracle with the W8A16 tolerance form."""
+    rng = np.random.default_rng(m + n)
+    qa = rng.choice(np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8),
+                    size=(m, k))
+    w = datagen.make_problem(1, n, k, seed=n + k).w
+    sa = np.exp2(rng.uniform(-10, 2, size=(m, k // 128))).astype(np.float32)
+    sw = np.exp2(rng.uniform(-12, -4, size=((n + 127) // 128, k // 128))).astype(np.float32)
+    c = run_w8a8(w8, qa, sa, w, sw, m, n, k, k, n, m)
+    rows, cols = datagen.sample_indices(m, n, 2000, seed=9)
+    oc, _, bound = oracle.gemm_w8a8_at(qa, sa, w, sw, m, n, k, rows, cols)
+    assert oracle.within_tolerance(c[rows, cols], oc, bound).all()
+
+
+def test_quantize_then_w8a8_pipeline(w8):
+    """BF16 activations -> GPU quantizer -> GPU W8A8 GEMM, against the
+    oracle's quantizer and W8A8 GEMM: identical codes and scales, outputs
+    within tolerance."""
+    m, n, k = 24, 3000, 2048
+    p = datagen.make_problem(m, n, k, seed=41)
+    a = dev_u16(p.a)
+    q = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    s = torch.empty((m, k // 128), dtype=torch.float32, device="cuda")
+    assert w8.act_quant_fp8_raw(a.data_ptr(), k, q.data_ptr(), k, s.data_ptr(), m, k) == 0
+    ww, sw = dev(p.w), dev(p.scale)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    w8.gemm_w8a8(q, s, ww, sw, c)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.act_quant(p.a, m, k)
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+    oc, _, bound = oracle.gemm_w8a8(oq, os_, p.w, p.scale, m, n, k)
+    g = c.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert oracle.within_tolerance(g, oc, bound).all()
+    # and the torch wrappers agree with the raw entry points
+    q2, s2 = w8.act_quant_fp8(dev_u16(p.a).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q) and torch.equal(s2, s)
