@@ -242,17 +242,43 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_ring_kernel(GemmArgs g)
     for (int b = 0; b < MB; ++b)
         red[(wave * MB + b) * 64 + lane] = acc[b];
     barrier_lds();
-    for (uint32_t pi = wave; pi < (uint32_t)(NBW * MB); pi += WAVES) {
-        const uint32_t j = pi / MB, b = pi % MB;
-        f32x4_t v[S::WK];
+    if constexpr (NBW * MB < WAVES) {
+        // Fewer output tiles than waves: every thread adds one output's WK
+        // partials (same wave order, same bits), so the tail is not left
+        // to NBW * MB waves.
+        constexpr uint32_t F = NBW * MB * 256u;
+        const float *redf = reinterpret_cast<const float *>(lds);
+        for (uint32_t f = threadIdx.x; f < F; f += WAVES * 64u) {
+            // float f: component f % 4 of lane (f % 256) / 4 of pair f / 256
+            const uint32_t pi = f / 256u, within = f % 256u, ln = within / 4u;
+            const uint32_t j = pi / MB, b = pi % MB;
+            float v[S::WK];
 #pragma unroll
-        for (int w = 0; w < S::WK; ++w)
-            v[w] = red[((j * S::WK + w) * MB + b) * 64 + lane];
-        f32x4_t sum = v[0];
+            for (int w = 0; w < S::WK; ++w)
+                v[w] = redf[((j * S::WK + w) * MB + b) * 256u + within];
+            float sum = v[0];
 #pragma unroll
-        for (int w = 1; w < S::WK; ++w)
-            sum += v[w];
-        store_c4(g, sum, m0 + 16u * b + rr, n0 + 16u * j + 4u * gq);
+            for (int w = 1; w < S::WK; ++w)
+                sum += v[w];
+            const uint32_t row = m0 + 16u * b + (ln & 15u);
+            const uint32_t col = n0 + 16u * j + 4u * (ln >> 4) + f % 4u;
+            if (row < g.m && col < g.n)
+                reinterpret_cast<uint16_t *>(g.c)[(size_t)row * g.c_stride + col] =
+                    (uint16_t)f32_to_bf16_bits(sum);
+        }
+    } else {
+        for (uint32_t pi = wave; pi < (uint32_t)(NBW * MB); pi += WAVES) {
+            const uint32_t j = pi / MB, b = pi % MB;
+            f32x4_t v[S::WK];
+#pragma unroll
+            for (int w = 0; w < S::WK; ++w)
+                v[w] = red[((j * S::WK + w) * MB + b) * 64 + lane];
+            f32x4_t sum = v[0];
+#pragma unroll
+            for (int w = 1; w < S::WK; ++w)
+                sum += v[w];
+            store_c4(g, sum, m0 + 16u * b + rr, n0 + 16u * j + 4u * gq);
+        }
     }
 }
 

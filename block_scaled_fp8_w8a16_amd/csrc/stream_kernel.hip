@@ -281,10 +281,37 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     const uint32_t out_col_off = 4u * (lane >> 4);
 
     if (g.splits == 1) {
-        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
-            const f32x4_t s = sum_waves<WAVES, P>(red, pi, lane);
-            const uint32_t j = pi / MB, b = pi % MB;
-            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+        if constexpr (P < WAVES) {
+            // Fewer output tiles than waves: spread the sums over all the
+            // workgroup's threads, one output each (same wave order, so the
+            // same bits), instead of leaving them to P waves (measured
+            // 6.15 -> 5.87 us at 8 x 4096 x 4096, one tile of 16 waves).
+            constexpr uint32_t F = P * 256u;   // floats per partial set
+            const float *redf = reinterpret_cast<const float *>(lds);
+            for (uint32_t f = threadIdx.x; f < F; f += WAVES * 64u) {
+                float v[WAVES];
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w)
+                    v[w] = redf[w * F + f];
+                float sum = v[0];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w)
+                    sum += v[w];
+                // float f is component f % 4 of lane (f % 256) / 4 of tile f / 256
+                const uint32_t pi = f / 256u, ln = (f % 256u) / 4u;
+                const uint32_t j = pi / MB, b = pi % MB;
+                const uint32_t row = m0 + 16u * b + (ln & 15u);
+                const uint32_t col = n0 + 16u * j + 4u * (ln >> 4) + f % 4u;
+                if (row < g.m && col < g.n)
+                    reinterpret_cast<uint16_t *>(g.c)[(size_t)row * g.c_stride + col] =
+                        (uint16_t)f32_to_bf16_bits(sum);
+            }
+        } else {
+            for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+                const f32x4_t s = sum_waves<WAVES, P>(red, pi, lane);
+                const uint32_t j = pi / MB, b = pi % MB;
+                store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+            }
         }
         return;
     }

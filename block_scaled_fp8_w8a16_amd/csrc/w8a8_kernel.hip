@@ -250,13 +250,37 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_w8a8_kernel(GemmArgs g, cons
         for (int b = 0; b < MB; ++b)
             red[(wave * P + j * MB + b) * 64 + lane] = acc[j][b];
     __syncthreads();
-    for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
-        f32x4_t s = red[pi * 64 + lane];
+    if constexpr (P < WAVES) {
+        // Fewer output tiles than waves: every thread adds one output's
+        // partials, in wave order.
+        constexpr uint32_t F = P * 256u;
+        const float *redf = reinterpret_cast<const float *>(lds);
+        for (uint32_t f = threadIdx.x; f < F; f += WAVES * 64u) {
+            float v[WAVES];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w)
-            s += red[(w * P + pi) * 64 + lane];
-        const uint32_t j = pi / MB, b = pi % MB;
-        store_c4(g, s, m0 + 16u * b + rr, n0 + 16u * j + 4u * gq);
+            for (int w = 0; w < WAVES; ++w)
+                v[w] = redf[w * F + f];
+            float sum = v[0];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                sum += v[w];
+            const uint32_t pi = f / 256u, ln = (f % 256u) / 4u;
+            const uint32_t j = pi / MB, b = pi % MB;
+            const uint32_t row = m0 + 16u * b + (ln & 15u);
+            const uint32_t col = n0 + 16u * j + 4u * (ln >> 4) + f % 4u;
+            if (row < g.m && col < g.n)
+                reinterpret_cast<uint16_t *>(g.c)[(size_t)row * g.c_stride + col] =
+                    (uint16_t)f32_to_bf16_bits(sum);
+        }
+    } else {
+        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+            f32x4_t s = red[pi * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                s += red[(w * P + pi) * 64 + lane];
+            const uint32_t j = pi / MB, b = pi % MB;
+            store_c4(g, s, m0 + 16u * b + rr, n0 + 16u * j + 4u * gq);
+        }
     }
 }
 
