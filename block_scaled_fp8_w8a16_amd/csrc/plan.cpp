@@ -71,7 +71,7 @@ static uint32_t div_up(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 {
     switch (mb * 100 + nb) {
-    case 101: case 102: case 104: case 108:
+    case 101: case 102: case 103: case 104: case 108:
     case 201: case 202: case 204:
     case 401: case 402:
         return true;
@@ -83,7 +83,7 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 static bool w8a8_shape_supported(uint32_t mb, uint32_t nb)
 {
     switch (mb * 100 + nb) {
-    case 101: case 102: case 104:
+    case 101: case 102: case 103: case 104:
     case 201: case 202: case 204:
     case 401: case 402:
         return true;
@@ -361,6 +361,18 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
                 break;
             }
         }
+        // 48-column tiles when they fill the CUs' last round of tiles
+        // clearly better than the choice above (12288 columns: 256 tiles of
+        // 48 instead of 192 of 64; measured 14.9 vs 15.4 us at 16 x 12288 x
+        // 5120).
+        auto occupancy = [&](uint32_t c) {
+            const uint64_t t = (uint64_t)div_up(nb16, c) * m_tiles;
+            const uint64_t rounds = (t + p.cu_count - 1) / p.cu_count;
+            return (double)t / (double)(rounds * p.cu_count);
+        };
+        if (stream_shape_supported(p.m_blocks, 3) && nbw > 1 &&
+            occupancy(3) > occupancy(nbw) + 0.1)
+            nbw = 3;
         p.n_blocks = nbw;
         const uint32_t pairs = p.m_blocks * p.n_blocks;
         p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
@@ -377,7 +389,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         // the ring kernel's row-contiguous LDS-DMA stages (measured 3-9 %);
         // below that, or with fewer rows, its slower start does not pay off.
         const uint32_t rmb = m <= 16 ? 1 : 2;
-        if (m >= 8 && m <= 32 && wbytes >= (48ull << 20) && p.splits == 1) {
+        if (m >= 8 && m <= 32 && wbytes >= (48ull << 20) && p.splits == 1 && nbw != 3) {
             const bool a8 = m <= 8;
             // 16 waves measured best for 16 rows x 64 columns, else 8; three
             // stages in flight unless LDS allows only two.
@@ -451,6 +463,16 @@ int make_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
             p.n_blocks = c;
             break;
         }
+    // 48-column tiles when they fill the CUs' last round of tiles clearly
+    // better (as for the stream kernel).
+    auto occupancy = [&](uint32_t c) {
+        const uint64_t t = (uint64_t)div_up(n, 16 * c) * m_tiles;
+        const uint64_t rounds = (t + p.cu_count - 1) / p.cu_count;
+        return (double)t / (double)(rounds * p.cu_count);
+    };
+    if (w8a8_shape_supported(p.m_blocks, 3) && p.n_blocks > 1 &&
+        occupancy(3) > occupancy(p.n_blocks) + 0.1)
+        p.n_blocks = 3;
     const uint32_t pairs = p.m_blocks * p.n_blocks;
     p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
     while (p.waves > 4 && (ksteps < 2 * p.waves ||

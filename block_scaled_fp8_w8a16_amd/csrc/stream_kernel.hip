@@ -428,6 +428,7 @@ hipError_t launch_stream_any(const Args &g, const w8a16_plan_t &p, hipStream_t s
     switch (p.m_blocks * 100 + p.n_blocks) {
     case 101: return launch_stream_mn<1, 1>(g, p, stream);
     case 102: return launch_stream_mn<1, 2>(g, p, stream);
+    case 103: return launch_stream_mn<1, 3>(g, p, stream);
     case 104: return launch_stream_mn<1, 4>(g, p, stream);
     case 108: return launch_stream_mn<1, 8>(g, p, stream);
     case 201: return launch_stream_mn<2, 1>(g, p, stream);

@@ -329,6 +329,7 @@ hipError_t launch_w8a8(const GemmArgs &g, const float *a_scales, const w8a16_pla
     switch (p.m_blocks * 100 + p.n_blocks) {
     case 101: return launch_w8a8_mn<1, 1>(g, a_scales, p, stream);
     case 102: return launch_w8a8_mn<1, 2>(g, a_scales, p, stream);
+    case 103: return launch_w8a8_mn<1, 3>(g, a_scales, p, stream);
     case 104: return launch_w8a8_mn<1, 4>(g, a_scales, p, stream);
     case 201: return launch_w8a8_mn<2, 1>(g, a_scales, p, stream);
     case 202: return launch_w8a8_mn<2, 2>(g, a_scales, p, stream);

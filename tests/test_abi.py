@@ -118,10 +118,12 @@ def test_default_plans_cover_the_problem(m, n, k):
 
 def test_small_m_plans_fill_the_chip():
     # weights under 48 MiB stream; 8..32 rows over a larger weight take the
-    # ring kernel
-    for m, n, k, kern in [(8, 4096, 4096, w8.KERNEL_STREAM), (16, 12288, 5120, w8.KERNEL_RING),
+    # ring kernel, unless 48-column stream tiles fill the CUs better
+    p = w8.plan(16, 12288, 5120)
+    assert (p.kernel, p.n_blocks, p.grid) == (w8.KERNEL_STREAM, 3, 256)
+    for m, n, k, kern in [(8, 4096, 4096, w8.KERNEL_STREAM), (16, 12288, 5120, w8.KERNEL_STREAM),
                           (32, 6144, 2048, w8.KERNEL_STREAM), (4, 14336, 4096, w8.KERNEL_STREAM),
-                          (8, 12288, 5120, w8.KERNEL_RING), (32, 8192, 8192, w8.KERNEL_RING)]:
+                          (16, 16384, 5120, w8.KERNEL_RING), (32, 8192, 8192, w8.KERNEL_RING)]:
         p = w8.plan(m, n, k)
         assert p.kernel == kern, (m, n, k)
         assert p.m_blocks == (1 if m <= 16 else 2)

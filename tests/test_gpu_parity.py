@@ -131,7 +131,7 @@ def test_exact_data_bit_exact_default_plan(w8, m, n, k):
     check_full(p, g, exact=True)
 
 
-STREAM_SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4),
+STREAM_SHAPES = [(1, 1), (1, 2), (1, 3), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4),
                  (4, 1), (4, 2)]
 
 
@@ -534,7 +534,7 @@ def run_w8a8(w8, qa, sa, w, sw, m, n, k, qa_row_stride, c_row_stride, c_rows, pl
     return c.cpu().numpy().view(np.uint16)
 
 
-W8A8_VARIANTS = [(1, 1, 4), (1, 1, 8), (1, 1, 16), (1, 2, 8), (1, 2, 16), (1, 4, 4),
+W8A8_VARIANTS = [(1, 1, 4), (1, 1, 8), (1, 1, 16), (1, 2, 8), (1, 2, 16), (1, 3, 8), (1, 4, 4),
                  (1, 4, 8), (2, 1, 8), (2, 1, 16), (2, 2, 8), (2, 4, 4), (2, 4, 8),
                  (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 2, 8)]
 
