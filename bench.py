@@ -264,7 +264,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, wl_name: str, command: str
         fh.write("fetch_scale: %.4f\n" % f_scale)
         fh.write("write_scale: %.4f\n" % w_scale)
         for k, n, f, w, b in lines:
-            short = k.split("(")[0].replace("void ", "").split("::")[-1]
+            short = k.replace("void ", "").replace("w8a16::(anonymous namespace)::", "")
+            short = short.split("(")[0]
             fh.write("kernel %s: dispatches %d, fetch_kib_raw %.1f, write_kib_raw %.1f, "
                      "hbm_bytes %.0f\n" % (short, n, f, w, b))
         fh.write("hbm_bytes_per_launch: %.0f\n" % total)
@@ -541,9 +542,14 @@ def main():
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         wl_name = sys.argv[3] if len(sys.argv) > 3 else MAIN_WORKLOAD
-        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- python3 "
-               "bench.py --steps 50 --warmup 5 --no-cpu --only-main --workload %s ; "
-               "python3 bench.py --summarize-trace TRACE_DIR %s" % (wl_name, wl_name))
+        if wl_name in ("batched", "w8a8"):       # the --batched / --w8a8 legs
+            cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- "
+                   "python3 bench.py --%s ; python3 bench.py --summarize-trace TRACE_DIR %s"
+                   % (wl_name, wl_name))
+        else:
+            cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- "
+                   "python3 bench.py --steps 50 --warmup 5 --no-cpu --only-main --workload %s ; "
+                   "python3 bench.py --summarize-trace TRACE_DIR %s" % (wl_name, wl_name))
         summarize_trace(sys.argv[2], wl_name, cmd)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-run":
