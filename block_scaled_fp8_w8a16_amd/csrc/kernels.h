@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "w8a16.h"
 
 namespace w8a16 {
@@ -39,6 +41,29 @@ struct QuantArgs {
     float *scales;
     uint32_t a_stride, q_stride, m, k;
 };
+
+// A launch of `kern` needs `bytes` of dynamic LDS: above the 64 KiB
+// default, raise the kernel's limit to `limit` (the most any plan uses) on
+// the current device.  The attribute is per device, so it is set once per
+// device id (bit i of `done`; ids of 64 and above are set on every call).
+inline hipError_t allow_lds(const void *kern, uint32_t bytes, uint32_t limit,
+                            std::atomic<uint64_t> &done)
+{
+    if (bytes <= 65536)
+        return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(limit > bytes ? limit : bytes));
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_act_quant(const QuantArgs &q, hipStream_t stream);

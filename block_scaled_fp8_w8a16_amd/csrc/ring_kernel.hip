@@ -290,15 +290,11 @@ hipError_t launch_ring_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
         return hipErrorInvalidValue;
     } else {
         auto kern = w8a16_ring_kernel<MB, NBW, SK, NST, WAVES, A8>;
-        static bool attr_set = false;
-        if (p.lds_bytes > 65536 && !attr_set) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kMaxLdsBytes);
-            if (e != hipSuccess)
-                return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes,
+                                 kMaxLdsBytes, lds_set);
+        if (e != hipSuccess)
+            return e;
         hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g);
         return hipGetLastError();
     }

@@ -50,6 +50,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace w8a16 {
 
@@ -375,15 +376,11 @@ hipError_t launch_stream_t(const Args &g, const w8a16_plan_t &p, hipStream_t str
         kern = w8a16_stream_batched_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
     else
         kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
-    static bool attr_set = false;
-    if (p.lds_bytes > 65536 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)p.lds_bytes);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes, kMaxLdsBytes,
+                             lds_set);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g);
     return hipGetLastError();
 }

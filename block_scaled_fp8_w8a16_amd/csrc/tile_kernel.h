@@ -411,17 +411,13 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
         return hipErrorInvalidValue;
     } else {
     auto kern = w8a16_tile_kernel<MT, NT, WST, AST, KH, PROD>;
-    static bool attr_set = false;
-    if (p.lds_bytes > 65536 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)p.lds_bytes);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes, kMaxLdsBytes,
+                             lds_set);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1)
         return e;
     const uint32_t ws_cols = p.n_tiles * NT;

@@ -302,13 +302,13 @@ hipError_t launch_w8a8_mn(const GemmArgs &g, const float *a_scales, const w8a16_
         break;
     default: return hipErrorInvalidValue;
     }
-    if (p.lds_bytes > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)p.lds_bytes);
-        if (e != hipSuccess)
-            return e;
-    }
+    // one flag set per (MB, NBW) instantiation, covering its three wave counts
+    static std::atomic<uint64_t> lds_set[3];
+    const int wi = p.waves == 4 ? 0 : (p.waves == 8 ? 1 : 2);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes, kMaxLdsBytes,
+                             lds_set[wi]);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g, a_scales);
     return hipGetLastError();
 }
