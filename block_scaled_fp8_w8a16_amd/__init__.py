@@ -315,7 +315,7 @@ def act_quant_fp8(a, *, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     a_rs = a.stride(0) if m > 1 else max(a.stride(0), k)
-    _raise_if(act_quant_fp8_raw(a.data_ptr(), a_rs, q.data_ptr(), k if k % 16 == 0 else k,
+    _raise_if(act_quant_fp8_raw(a.data_ptr(), a_rs, q.data_ptr(), k,
                                 s.data_ptr(), m, k, stream.cuda_stream))
     return q, s
 

@@ -24,8 +24,9 @@
  * by the caller, who keeps the buffers alive until the stream has passed
  * the call.  The library keeps no pointer to them.  It owns one split-K
  * workspace and counter array per (device, stream), allocated with
- * hipMalloc on first use and grown when a larger plan needs it; make one
- * call on a stream before capturing that stream into a HIP graph.
+ * hipMalloc on first use and grown when a larger plan needs it (growing
+ * first waits for the stream); make one call on a stream before capturing
+ * that stream into a HIP graph.
  *
  * Alignment and aliasing: A, W, S and C must be 16-byte aligned (torch
  * allocations are).  C must not overlap A, W or S.  c_row_stride may be any
