@@ -289,10 +289,13 @@ def test_m_sweep(w8):
 
 
 @pytest.mark.parametrize("m,n,k", [(96, 4096, 4096), (192, 2048, 8192), (24, 8192, 8192),
-                                   (48, 4096, 4096)])
+                                   (48, 4096, 4096), (48, 8192, 8192), (40, 6144, 4096),
+                                   (8, 12288, 5120), (65, 8192, 8192)])
 def test_default_plans_at_size_sampled(w8, m, n, k):
     """Default plans of the M sweep's larger shapes (64-column tiles, two row
-    tiles, ring with two row blocks, stream with four), sampled parity."""
+    tiles, ring with two row blocks, stream with four, one 64-row tile for
+    33..64 rows over a large weight, two for 65 rows, 48-column stream
+    tiles), sampled parity."""
     p = datagen.make_problem(m, n, k, seed=m + n + k, c_extra_rows=1)
     g = run_gpu(w8, p)
     rows, cols = datagen.sample_indices(m, n, 300, seed=5)
