@@ -15,7 +15,7 @@
  *   C  BF16  [M, c_row_stride]   only the first N elements of each row are written
  *
  * The scale of a block is applied once to that block's 128-wide partial dot
- * product (the "fold point" of one FP8 scale block per K step), never to
+ * product (the fold point of one FP8 scale block per K step), never to
  * single weights.  Everything is accumulated in IEEE double and rounded once,
  * directly from double, to BF16 with round-to-nearest-even.
  *
