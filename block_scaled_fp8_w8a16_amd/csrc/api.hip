@@ -36,6 +36,9 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::mutex g_cu_mutex;
 std::map<int, uint32_t> g_cu_count;
 
+std::mutex g_rr_mutex;
+std::map<int, bool> g_round_robin;
+
 int hip_fail(hipError_t e, const char *what)
 {
     char buf[256];
@@ -57,6 +60,40 @@ int device_cu_count(int dev, uint32_t *out)
         return hip_fail(e, "hipDeviceGetAttribute");
     g_cu_count[dev] = (uint32_t)cus;
     *out = (uint32_t)cus;
+    return W8A16_OK;
+}
+
+// Whether device `dev` dispatches workgroup i to XCD i mod 8 (what the
+// XCD-local split publication relies on), from one probe grid per device
+// run on `stream` and waited for.  A device that does not, or a failed
+// probe, gets the device-scope publication.
+int device_round_robin(int dev, hipStream_t stream, bool *out)
+{
+    std::lock_guard<std::mutex> lock(g_rr_mutex);
+    auto it = g_round_robin.find(dev);
+    if (it != g_round_robin.end()) {
+        *out = it->second;
+        return W8A16_OK;
+    }
+    constexpr uint32_t kProbeGrid = 4096;
+    uint32_t *d = nullptr;
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&d), kProbeGrid * sizeof(uint32_t));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMalloc(XCD probe)");
+    static uint32_t h[kProbeGrid];
+    e = launch_xcc_probe(d, kProbeGrid, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h, d, sizeof h, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    (void)hipFree(d);
+    if (e != hipSuccess)
+        return hip_fail(e, "XCD dispatch probe");
+    bool ok = true;
+    for (uint32_t i = 0; i < kProbeGrid; ++i)
+        ok = ok && h[i] == (i & 7u);
+    g_round_robin[dev] = ok;
+    *out = ok;
     return W8A16_OK;
 }
 
@@ -128,7 +165,15 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
         if (st != W8A16_OK)
             return st;
     }
+    bool xcd_local = false;
+    if (plan.kernel == W8A16_KERNEL_STREAM && (plan.flags & W8A16_FLAG_XCD_LOCAL)) {
+        int st = device_round_robin(dev, stream, &xcd_local);
+        if (st != W8A16_OK)
+            return st;
+    }
     GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.xcd_local = xcd_local ? 1u : 0u;
     g.a = static_cast<const uint8_t *>(a);
     g.w = static_cast<const uint8_t *>(w_fp8);
     g.scale = block_scale;

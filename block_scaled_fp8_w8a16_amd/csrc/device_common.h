@@ -67,6 +67,31 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
     return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Id of the XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11));
+}
+
+// Arrival-count increment that marks a split published with the
+// device-scope release (the low 16 bits count arrivals).
+constexpr uint32_t kForeignArrival = 1u << 16;
+
+// 16-byte load that does not hit in this CU's L1 (two device-scope 8-byte
+// loads), for data another CU of the same XCD has just stored to the L2.
+__device__ __forceinline__ f32x4_t load_l2(const f32x4_t *p)
+{
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    f32x4_t v;
+    v.x = __builtin_bit_cast(float, (uint32_t)lo);
+    v.y = __builtin_bit_cast(float, (uint32_t)(lo >> 32));
+    v.z = __builtin_bit_cast(float, (uint32_t)hi);
+    v.w = __builtin_bit_cast(float, (uint32_t)(hi >> 32));
+    return v;
+}
+
 // LDS pointer type of the global_load_lds builtin (LDS DMA).
 typedef __attribute__((address_space(3))) void lds_void_t;
 

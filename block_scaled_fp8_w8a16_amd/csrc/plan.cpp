@@ -72,7 +72,7 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
 {
     switch (mb * 100 + nb) {
     case 101: case 102: case 103: case 104: case 108:
-    case 201: case 202: case 204:
+    case 201: case 202: case 204: case 208:
     case 401: case 402:
         return true;
     default:
@@ -128,7 +128,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             snprintf(buf, sizeof buf, "w8a16_plan: depth=%u must be 1, 2 or 4", p->depth);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->flags & ~(uint32_t)W8A16_FLAG_DIRECT) {
+        if (p->flags & ~(uint32_t)(W8A16_FLAG_DIRECT | W8A16_FLAG_XCD_LOCAL)) {
             snprintf(buf, sizeof buf, "w8a16_plan: unknown flags 0x%x", p->flags);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
@@ -269,6 +269,19 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         return fail(W8A16_ERR_BAD_PLAN, buf);
     }
     p->grid = (uint32_t)grid;
+    if (p->flags & W8A16_FLAG_XCD_LOCAL) {
+        // The splits of a tile are consecutive logical workgroups, and each
+        // XCD runs a contiguous range of grid / 8 of them: the ranges must
+        // hold whole tiles.
+        if (p->kernel != W8A16_KERNEL_STREAM || p->splits < 2 || p->grid % 8 != 0 ||
+            (p->grid / 8) % p->splits != 0) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: XCD-local split publication needs the stream kernel, "
+                     "splits >= 2 and a grid of 8 equal ranges of whole tiles (splits=%u, "
+                     "grid=%u)", p->splits, p->grid);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+    }
     if (p->splits > 1 && p->kernel == W8A16_KERNEL_TILE) {
         // whole FP32 tiles per split, added by a second kernel
         p->workspace_bytes = (uint64_t)p->splits * p->m_tiles * 16 * p->m_blocks *
@@ -276,7 +289,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         p->counter_count = 0;
     } else if (p->splits > 1) {
         p->workspace_bytes = grid * (uint64_t)p->m_blocks * p->n_blocks * kAccBytes;
-        p->counter_count = (uint32_t)tiles;
+        p->counter_count = (uint32_t)tiles * kCounterStride;
     } else {
         p->workspace_bytes = 0;
         p->counter_count = 0;
@@ -379,11 +392,32 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         while (p.waves > 4 && ksteps < 2 * p.waves)
             p.waves /= 2;
         const uint32_t tiles = div_up(nb16, nbw) * m_tiles;
-        // Split K only when the tiles would leave most CUs idle and every
-        // split still gives each wave two or more K steps.
+        // Split K only when the tiles would leave most CUs idle, and only
+        // with XCD-local publication (the device-scope release of a split
+        // partial measured 40-90 us per call over such grids).  Splits
+        // double while the grid fits the CUs, each split keeps 8 or more K
+        // steps and every XCD's range of the grid holds whole tiles; a
+        // split of 32 or more steps keeps 16 waves, shorter ones take 8
+        // (measured on MI355X, us per call: 1 x 1024 x 8192 48.9 -> 5.6,
+        // 16 x 1024 x 8192 50.1 -> 6.2, 4 x 2048 x 14336 95.2 -> 8.6,
+        // 8 x 512 x 8192 7.4 unsplit -> 5.4).
+        auto xcd_whole = [&](uint32_t sp) {
+            const uint32_t grid = tiles * sp;
+            return grid % 8 == 0 && (grid / 8) % sp == 0;
+        };
         p.splits = 1;
-        while (tiles * p.splits * 2 <= p.cu_count && ksteps >= 4 * p.waves * p.splits)
-            p.splits *= 2;
+        if (tiles * 2 <= p.cu_count) {
+            while (tiles * p.splits * 2 <= p.cu_count && ksteps / (p.splits * 2) >= 8 &&
+                   xcd_whole(p.splits * 2))
+                p.splits *= 2;
+        }
+        if (p.splits > 1) {
+            p.flags |= W8A16_FLAG_XCD_LOCAL;
+            const uint32_t sps = div_up(ksteps, p.splits);
+            const uint32_t wmax = sps >= 32 ? 16u : 8u;
+            if (p.waves > wmax)
+                p.waves = wmax;
+        }
 
         // A large weight (>= 48 MiB) with 8..32 rows streams faster through
         // the ring kernel's row-contiguous LDS-DMA stages (measured 3-9 %);

@@ -16,7 +16,10 @@ constexpr uint32_t kDefaultCUs = 256;            // MI355X
 // Dynamic LDS a plan may use: the 160 KiB of a gfx950 CU less room for the
 // kernels' small static __shared__ variables.
 constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 256;
-constexpr uint32_t kTileMaxSteps = 64;           // tile kernel: K steps per split (one per lane)
+constexpr uint32_t kTileMaxSteps = 64;
+// Split-K arrival counters sit 256 bytes apart (one per tile), so that no
+// two tiles' atomics meet in one cache line.
+constexpr uint32_t kCounterStride = 64;           // tile kernel: K steps per split (one per lane)
 
 // LDS of the tile kernel for a (16 * m_blocks) x (16 * n_blocks) C tile:
 // a_stages buffers of one K step of A (16 * m_blocks rows x 256 bytes of

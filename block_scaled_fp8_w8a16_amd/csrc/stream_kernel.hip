@@ -318,29 +318,56 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     }
 
     // ---- split-K: publish this split's tile, the last arrival adds all ----
+    // Device-scope publication: a release (L2 writeback) before the arrival
+    // count and an acquire after it, so splits may run on any XCD.
+    // XCD-local publication: all splits of the tile run on one XCD (the
+    // logical ids of a tile's splits are consecutive and the host made each
+    // XCD's share of ids a whole number of tiles), so their partials meet in
+    // that XCD's L2; a split only waits until its stores have reached the
+    // L2, and the last one reads them past its own L1.  A workgroup that
+    // finds itself on another XCD than round-robin dispatch puts it (read
+    // from the hardware register) publishes with the device-scope release,
+    // and its arrival is marked so that the last split acquires too.
+    const bool foreign = g.xcd_local && xcc_id() != (blockIdx.x & 7u);
+    const bool local = g.xcd_local && !foreign;
     f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES)
         ws_tile[((size_t)split * P + pi) * 64 + lane] = sum_waves<WAVES, P>(red, pi, lane);
-    __threadfence();
+    if (local)
+        wait_vm<0>();
+    else
+        __threadfence();
     __syncthreads();
     __shared__ uint32_t last;
     if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(g.counters + tile, 1u);
-        last = (prev == g.splits - 1u) ? 1u : 0u;
+        const uint32_t add = foreign ? 1u + kForeignArrival : 1u;
+        const uint32_t now = atomicAdd(g.counters + (size_t)tile * kCounterStride, add) + add;
+        last = (now & (kForeignArrival - 1u)) == g.splits ? (now >= kForeignArrival ? 2u : 1u)
+                                                             : 0u;
     }
     __syncthreads();
     if (!last)
         return;
-    __threadfence();
-    for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
-        f32x4_t s = ws_tile[pi * 64 + lane];
-        for (uint32_t sp = 1; sp < g.splits; ++sp)
-            s += ws_tile[((size_t)sp * P + pi) * 64 + lane];
-        const uint32_t j = pi / MB, b = pi % MB;
-        store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+    if (!g.xcd_local || last == 2u || foreign) {
+        __threadfence();
+        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+            f32x4_t s = ws_tile[pi * 64 + lane];
+            for (uint32_t sp = 1; sp < g.splits; ++sp)
+                s += ws_tile[((size_t)sp * P + pi) * 64 + lane];
+            const uint32_t j = pi / MB, b = pi % MB;
+            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+        }
+    } else {
+        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+            f32x4_t s = load_l2(ws_tile + pi * 64 + lane);
+            for (uint32_t sp = 1; sp < g.splits; ++sp)
+                s += load_l2(ws_tile + ((size_t)sp * P + pi) * 64 + lane);
+            const uint32_t j = pi / MB, b = pi % MB;
+            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
+        }
     }
     if (threadIdx.x == 0)
-        atomicExch(g.counters + tile, 0u);   // ready for the next call on this stream
+        atomicExch(g.counters + (size_t)tile * kCounterStride, 0u);   // ready for the next call on this stream
 }
 
 template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
@@ -431,13 +458,26 @@ hipError_t launch_stream_any(const Args &g, const w8a16_plan_t &p, hipStream_t s
     case 201: return launch_stream_mn<2, 1>(g, p, stream);
     case 202: return launch_stream_mn<2, 2>(g, p, stream);
     case 204: return launch_stream_mn<2, 4>(g, p, stream);
+    case 208: return launch_stream_mn<2, 8>(g, p, stream);
     case 401: return launch_stream_mn<4, 1>(g, p, stream);
     case 402: return launch_stream_mn<4, 2>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
+__global__ __launch_bounds__(64) void w8a16_xcc_probe_kernel(uint32_t *out)
+{
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = xcc_id();
+}
+
 }  // namespace
+
+hipError_t launch_xcc_probe(uint32_t *out, uint32_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(w8a16_xcc_probe_kernel, dim3(grid), dim3(64), 0, stream, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {

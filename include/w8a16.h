@@ -101,7 +101,8 @@ typedef struct w8a16_plan {
     uint32_t block;           /* threads per workgroup (derived) */
     uint32_t lds_bytes;       /* LDS per workgroup (derived) */
     uint64_t workspace_bytes; /* split-K FP32 partials (derived; 0 if splits == 1) */
-    uint32_t counter_count;   /* split-K arrival counters (derived) */
+    uint32_t counter_count;   /* 32-bit words of split-K arrival counters, one counter
+                                 per tile every 64 words (derived) */
     uint32_t cu_count;        /* compute units the plan was sized for */
     uint32_t depth;           /* stream: K steps each wave keeps in flight (1, 2, 4);
                                  tile: weight ring buffers; ring: stages in flight (2..4) */
@@ -120,7 +121,15 @@ enum {
     W8A16_FLAG_DIRECT = 1u,
     /* Ring kernel, m <= 8 with m_blocks == 1: stage 8 A rows instead of 16
      * (derived by w8a16_plan_finalize from m; callers need not set it). */
-    W8A16_FLAG_A8 = 2u
+    W8A16_FLAG_A8 = 2u,
+    /* Stream kernel with splits > 1: the K splits of a tile publish their
+     * FP32 partials through the L2 of the XCD they all run on, with no
+     * device-wide release (a device-scope release writes back the whole L2
+     * and costs microseconds over a grid).  Needs the grid to be a multiple
+     * of 8 with a whole number of tiles' splits per XCD; the library checks
+     * once per device that workgroups are dispatched round-robin over the
+     * XCDs and uses the device-scope path where they are not. */
+    W8A16_FLAG_XCD_LOCAL = 4u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

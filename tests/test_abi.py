@@ -111,7 +111,7 @@ def test_default_plans_cover_the_problem(m, n, k):
         assert p.counter_count == 0
     elif p.splits > 1:
         assert p.workspace_bytes == p.grid * p.m_blocks * p.n_blocks * 1024
-        assert p.counter_count == p.m_tiles * p.n_tiles
+        assert p.counter_count == p.m_tiles * p.n_tiles * 64
     else:
         assert p.workspace_bytes == 0
 
@@ -237,6 +237,49 @@ def test_split_k_only_when_tiles_leave_cus_idle():
     p = w8.plan(1, 128, 65536)
     assert p.splits > 1 and p.grid <= 256
     _covers(p, 1, 128, 65536)
+    # splits always publish XCD-locally: 8 equal ranges of whole tiles
+    assert p.flags & w8.FLAG_XCD_LOCAL
+    assert p.grid % 8 == 0 and (p.grid // 8) % p.splits == 0
+    # tiles that fill the CUs are not split
+    p = w8.plan(8, 4096, 4096)
+    assert p.splits == 1 and p.flags == 0
+
+
+@pytest.mark.parametrize("m,n,k,splits,waves", [
+    (1, 1024, 8192, 4, 8),      # 64 tiles x 4 splits of 16 steps
+    (16, 1024, 8192, 4, 8),
+    (4, 2048, 14336, 2, 16),    # 128 tiles x 2 splits of 56 steps
+    (8, 512, 8192, 8, 8),       # 32 tiles x 8 splits of 8 steps
+    (8, 512, 4096, 4, 8),       # 32 tiles x 4 splits of 8 steps
+    (16, 1536, 5120, 2, 8),     # 96 tiles x 2 splits of 20 steps
+    (32, 768, 2048, 2, 8),      # 48 tiles x 2 splits of 8 steps
+    (1, 100, 8192, 1, 16),      # 7 tiles: no split keeps XCD ranges whole
+])
+def test_split_rule_narrow_n(m, n, k, splits, waves):
+    p = w8.plan(m, n, k)
+    _covers(p, m, n, k)
+    assert (p.kernel, p.splits, p.waves) == (w8.KERNEL_STREAM, splits, waves)
+    assert bool(p.flags & w8.FLAG_XCD_LOCAL) == (splits > 1)
+    assert p.steps_per_split >= 8 or splits == 1
+
+
+def test_xcd_local_plans_need_whole_tiles_per_xcd():
+    # 48 tiles x 2 splits: 12 ids per XCD, 6 whole tiles each
+    p = w8.make_plan(32, 768, 2048, w8.KERNEL_STREAM, 2, 1, 2, depth=1,
+                     flags=w8.FLAG_XCD_LOCAL, waves=8)
+    assert p.grid == 96 and p.flags == w8.FLAG_XCD_LOCAL
+    bad = [(32, 768, 2048, 2, 1, 1),      # no split
+           (8, 100, 4096, 1, 1, 2),       # 7 tiles x 2 = 14: not a multiple of 8
+           (8, 192, 4096, 1, 1, 4)]       # 12 tiles x 4 = 48: 6 ids per XCD, 1.5 tiles
+    for m, n, k, mb, nb, sp in bad:
+        with pytest.raises(w8.W8A16Error) as e:
+            w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, sp, depth=1,
+                         flags=w8.FLAG_XCD_LOCAL, waves=8)
+        assert e.value.status == w8.ERR_BAD_PLAN and "XCD" in str(e.value)
+    # other kernels take no XCD-local flag
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 4, 8, 2, depth=4,
+                     flags=w8.FLAG_XCD_LOCAL, waves=8)
 
 
 def test_explicit_plans():

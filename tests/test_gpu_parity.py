@@ -153,6 +153,69 @@ def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, wave
     check_full(p, g, exact=True)
 
 
+def run_gpu_pair(w8, p1, p2, plan, stream):
+    """Both problems enqueued back to back on `stream` with one plan (one
+    split workspace), then one synchronisation; returns both C buffers."""
+    bufs = []
+    for prob in (p1, p2):
+        a, w, s, c = dev_u16(prob.a), dev(prob.w), dev(prob.scale), dev_u16(prob.c)
+        bufs.append((a, w, s, c))
+    torch.cuda.synchronize()
+    for prob, (a, w, s, c) in zip((p1, p2), bufs):
+        st = w8.gemm_raw(a.data_ptr(), prob.a_row_stride, w.data_ptr(), s.data_ptr(),
+                         c.data_ptr(), prob.c_row_stride, prob.m, prob.n, prob.k,
+                         stream.cuda_stream, plan)
+        assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    return [c.cpu().numpy().view(np.uint16).reshape(prob.c.shape)
+            for prob, (_, _, _, c) in zip((p1, p2), bufs)]
+
+
+XCD_SHAPES = STREAM_SHAPES + [(2, 8)]
+
+
+@pytest.mark.parametrize("mb,nb", XCD_SHAPES)
+@pytest.mark.parametrize("splits,ksteps", [(2, 16), (4, 13), (8, 64)])
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
+    """XCD-local split publication: 8 tiles (one per XCD range), two
+    different problems back to back on one stream, so a partial read
+    before its writer's stores reached the L2 (or a stale one from the
+    previous call) breaks bit exactness."""
+    m, n, k = 16 * mb - 3, 16 * nb * 8 - 5, 128 * ksteps
+    p1 = exact_problem(m, n, k, seed=7000 + 100 * mb + 10 * nb + splits + waves)
+    p2 = exact_problem(m, n, k, seed=9000 + 100 * mb + 10 * nb + splits + waves)
+    try:
+        plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1,
+                            flags=w8.FLAG_XCD_LOCAL, waves=waves)
+    except w8.W8A16Error as e:
+        assert e.status == w8.ERR_BAD_PLAN and "LDS" in str(e)
+        pytest.skip("variant needs more LDS than a CU has")
+    assert plan.grid == 8 * plan.splits and plan.flags == w8.FLAG_XCD_LOCAL
+    g1, g2 = run_gpu_pair(w8, p1, p2, plan, torch.cuda.Stream())
+    check_full(p1, g1, exact=True)
+    check_full(p2, g2, exact=True)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 8192), (16, 1024, 8192), (4, 2048, 14336),
+                                   (8, 512, 8192), (16, 1536, 5120), (32, 768, 2048),
+                                   (1, 128, 65536)])
+def test_default_split_plans_at_size_sampled(w8, m, n, k):
+    """Default plans that split K (narrow N, XCD-local publication): two
+    problems back to back on one stream, sampled parity of both."""
+    plan = w8.plan(m, n, k)
+    assert plan.splits > 1 and plan.flags & w8.FLAG_XCD_LOCAL
+    p1 = datagen.make_problem(m, n, k, seed=m + n + k, c_extra_rows=1)
+    p2 = datagen.make_problem(m, n, k, seed=m + n + k + 1, c_extra_rows=1)
+    g1, g2 = run_gpu_pair(w8, p1, p2, None, torch.cuda.Stream())
+    rows, cols = datagen.sample_indices(m, n, 300, seed=6)
+    for p, g in ((p1, g1), (p2, g2)):
+        oc, _, bound = oracle.gemm_at(p.a, p.w, p.scale, m, n, k, rows, cols,
+                                      a_row_stride=p.a_row_stride)
+        assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+        assert (g[m:, :] == p.c[m:, :]).all()
+
+
 RING_SHAPES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)]
 
 
