@@ -362,7 +362,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.depth = 1;
         p.flags = 0;
         p.m_blocks = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-        const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
+        uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
         const uint32_t fill = (3 * p.cu_count) / 4;
         uint32_t nbw = 1;
         const uint32_t cands[3] = {4, 2, 1};
@@ -386,6 +386,29 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         if (stream_shape_supported(p.m_blocks, 3) && nbw > 1 &&
             occupancy(3) > occupancy(nbw) + 0.1)
             nbw = 3;
+        // 17..32 rows: a CU's time goes with the bytes it requests (A rows
+        // plus weight rows of its tiles, times its rounds of tiles), so
+        // take the 16- or 32-row tile that needs the fewest (32 x 6144 x
+        // 2048: two 16 x 48 row tiles over 256 CUs, 7.06 us, against one
+        // 32 x 32 tile over 192 CUs, 7.43 us; 16 x 64 and 16 x 32 tiles
+        // 7.56 and 8.11 us, in the model's order).  Weights of 48 MiB and
+        // more go to the ring kernel below, which keeps 32-row blocks.
+        if (m > 16 && m <= 32 && wbytes < (48ull << 20)) {
+            auto cost = [&](uint32_t mb, uint32_t nb) {
+                const uint64_t t = (uint64_t)div_up(m, 16 * mb) * div_up(nb16, nb);
+                return (t + p.cu_count - 1) / p.cu_count * (32ull * mb + 16ull * nb);
+            };
+            uint64_t best = cost(p.m_blocks, nbw);
+            const uint32_t mbs[2] = {2, 1}, nbs[5] = {8, 4, 3, 2, 1};
+            for (uint32_t mb : mbs)
+                for (uint32_t nb : nbs)
+                    if (stream_shape_supported(mb, nb) && cost(mb, nb) < best) {
+                        best = cost(mb, nb);
+                        p.m_blocks = mb;
+                        nbw = nb;
+                    }
+            m_tiles = div_up(m, 16 * p.m_blocks);
+        }
         p.n_blocks = nbw;
         const uint32_t pairs = p.m_blocks * p.n_blocks;
         p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);

@@ -126,7 +126,9 @@ def test_small_m_plans_fill_the_chip():
                           (16, 16384, 5120, w8.KERNEL_RING), (32, 8192, 8192, w8.KERNEL_RING)]:
         p = w8.plan(m, n, k)
         assert p.kernel == kern, (m, n, k)
-        assert p.m_blocks == (1 if m <= 16 else 2)
+        # 17..32 rows stream as two 16-row tiles when that asks each CU for
+        # fewer bytes (32 x 6144 x 2048: 16 x 48 tiles); the ring keeps one
+        assert p.m_blocks == (1 if m <= 16 or kern == w8.KERNEL_STREAM else 2)
         assert p.grid >= 192          # at least three quarters of the 256 CUs
         assert p.splits == 1
         if kern == w8.KERNEL_RING:
@@ -231,6 +233,19 @@ def test_tile_plans_fill_the_cus_with_long_splits():
     assert w8.plan(48, 4096, 4096).kernel == w8.KERNEL_STREAM
     assert w8.plan(64, 6144, 2048).kernel == w8.KERNEL_STREAM
     assert w8.plan(33, 8192, 4096).kernel == w8.KERNEL_TILE
+
+
+@pytest.mark.parametrize("m,n,k,mb,nb", [
+    (32, 6144, 2048, 1, 3),     # 256 tiles of 16 x 48: 80 units per CU vs 96 for 32 x 32
+    (24, 4096, 4096, 1, 2),     # 256 tiles of 16 x 32: 64 vs 80 for 32 x 16
+    (17, 2048, 2048, 1, 1),     # 256 tiles of 16 x 16
+    (16, 6144, 2048, 1, 2),     # 16 rows: unchanged
+])
+def test_stream_tile_cost_model_17_to_32_rows(m, n, k, mb, nb):
+    p = w8.plan(m, n, k)
+    _covers(p, m, n, k)
+    assert (p.kernel, p.m_blocks, p.n_blocks) == (w8.KERNEL_STREAM, mb, nb)
+    assert p.m_tiles == -(-m // (16 * mb))
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():
