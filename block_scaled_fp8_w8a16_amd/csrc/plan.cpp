@@ -80,6 +80,39 @@ static bool stream_shape_supported(uint32_t mb, uint32_t nb)
     }
 }
 
+// Bytes (per 128 of K) a CU requests for a stream tile of mb 16-row and
+// nb 16-column blocks: the tile's A rows (BF16) and weight rows (FP8),
+// times the rounds of tiles each CU runs.
+static uint64_t stream_tile_cost(uint32_t m, uint32_t nb16, uint32_t cus, uint32_t mb,
+                                 uint32_t nb)
+{
+    const uint64_t t = (uint64_t)div_up(m, 16 * mb) * div_up(nb16, nb);
+    return (t + cus - 1) / cus * (32ull * mb + 16ull * nb);
+}
+
+struct StreamTile {
+    uint32_t mb, nb;
+    uint64_t cost;
+};
+
+// The stream tile with the lowest stream_tile_cost; ties go to more rows,
+// then more columns.  32 x 128 tiles are left out: they run only as four
+// waves, measured 1.9x slower than 32 x 64 tiles at the same rows.
+static StreamTile cheapest_stream_tile(uint32_t m, uint32_t nb16, uint32_t cus)
+{
+    StreamTile best = {0, 0, ~0ull};
+    const uint32_t mbs[3] = {4, 2, 1}, nbs[5] = {8, 4, 3, 2, 1};
+    for (uint32_t mb : mbs)
+        for (uint32_t nb : nbs) {
+            if (!stream_shape_supported(mb, nb) || (mb == 2 && nb == 8))
+                continue;
+            const uint64_t c = stream_tile_cost(m, nb16, cus, mb, nb);
+            if (c < best.cost)
+                best = {mb, nb, c};
+        }
+    return best;
+}
+
 static bool w8a8_shape_supported(uint32_t mb, uint32_t nb)
 {
     switch (mb * 100 + nb) {
@@ -311,12 +344,20 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     const uint32_t nb16 = div_up(n, 16);
 
     // Above 32 rows a weight larger than 16 MiB goes through the tile
-    // kernel (one L2 pass of the weight per 64-row tile); smaller weights
-    // and up to 64 rows stream faster (measured on MI355X: 48 x 8192 x 8192
-    // 22 vs 32 us, 48 x 4096 x 4096 12.4 vs 12.2 us, 40 x 6144 x 2048 11.1
-    // vs 10.2 us).
+    // kernel (one L2 pass of the weight per 64-row tile; measured on
+    // MI355X: 48 x 8192 x 8192 22 vs 32 us streaming).  Smaller weights
+    // stream up to 64 rows, and up to 128 rows while the stream tile that
+    // asks each CU for the fewest bytes needs one round of tiles
+    // (65 x 4096 x 4096 12.8 vs 15.6 us in the tile kernel, 128 x 4096 x
+    // 4096 14.9 vs 16.8, 96 x 2048 x 4096 9.9 vs 12.2; two rounds lose:
+    // 128 x 6144 x 2048 15.5 vs 12.2).
     const uint64_t wbytes = (uint64_t)n * k;
-    if (m > 64 || (m > 32 && wbytes > (16ull << 20))) {
+    StreamTile st16 = {1, 1, 0};
+    if (m > 16)
+        st16 = cheapest_stream_tile(m, nb16, p.cu_count);
+    const bool stream_fits = m <= 128 && wbytes <= (16ull << 20) &&
+                             (uint64_t)div_up(m, 16 * st16.mb) * div_up(nb16, st16.nb) <= p.cu_count;
+    if (m > 128 || (m > 32 && wbytes > (16ull << 20)) || (m > 64 && !stream_fits)) {
         // 64-row tiles up to 128 rows, 128-row tiles above (fewer weight
         // passes).  The grid is one workgroup per CU: K is split until the
         // tiles fill the CUs, with 128-column tiles when that leaves each
@@ -386,32 +427,33 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         if (stream_shape_supported(p.m_blocks, 3) && nbw > 1 &&
             occupancy(3) > occupancy(nbw) + 0.1)
             nbw = 3;
-        // 17..32 rows: a CU's time goes with the bytes it requests (A rows
+        // 17..64 rows: a CU's time goes with the bytes it requests (A rows
         // plus weight rows of its tiles, times its rounds of tiles), so
-        // take the 16- or 32-row tile that needs the fewest (32 x 6144 x
-        // 2048: two 16 x 48 row tiles over 256 CUs, 7.06 us, against one
-        // 32 x 32 tile over 192 CUs, 7.43 us; 16 x 64 and 16 x 32 tiles
-        // 7.56 and 8.11 us, in the model's order).  Weights of 48 MiB and
-        // more go to the ring kernel below, which keeps 32-row blocks.
-        if (m > 16 && m <= 32 && wbytes < (48ull << 20)) {
-            auto cost = [&](uint32_t mb, uint32_t nb) {
-                const uint64_t t = (uint64_t)div_up(m, 16 * mb) * div_up(nb16, nb);
-                return (t + p.cu_count - 1) / p.cu_count * (32ull * mb + 16ull * nb);
-            };
-            uint64_t best = cost(p.m_blocks, nbw);
-            const uint32_t mbs[2] = {2, 1}, nbs[5] = {8, 4, 3, 2, 1};
-            for (uint32_t mb : mbs)
-                for (uint32_t nb : nbs)
-                    if (stream_shape_supported(mb, nb) && cost(mb, nb) < best) {
-                        best = cost(mb, nb);
-                        p.m_blocks = mb;
-                        nbw = nb;
-                    }
+        // take the 16-, 32- or 64-row tile that needs the fewest.  Measured
+        // on MI355X (us per call, old tile -> chosen tile): 32 x 6144 x 2048
+        // 32 x 32 7.43 -> two 16 x 48 7.06; 48 x 4096 x 4096 64 x 16 12.19
+        // -> two 32 x 32 9.95; 40 x 6144 x 2048 64 x 32 10.12 -> two 32 x 64
+        // 8.66; 48 x 2048 x 4096 64 x 16 9.00 -> three 16 x 32 7.33; the
+        // other candidates in the model's order.  Weights of 48 MiB and
+        // more with up to 32 rows go to the ring kernel below, which keeps
+        // 32-row blocks.
+        bool by_cost = false;
+        if (m > 16 && wbytes < (48ull << 20)) {
+            if (stream_tile_cost(m, nb16, p.cu_count, st16.mb, st16.nb) <
+                stream_tile_cost(m, nb16, p.cu_count, p.m_blocks, nbw)) {
+                p.m_blocks = st16.mb;
+                nbw = st16.nb;
+            }
             m_tiles = div_up(m, 16 * p.m_blocks);
+            by_cost = true;
         }
         p.n_blocks = nbw;
         const uint32_t pairs = p.m_blocks * p.n_blocks;
         p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
+        // 32 x 64 tiles: 8 waves measured 7-8 % faster than 4 (40 x 6144 x
+        // 2048: 8.66 vs 9.35 us; 64 x 6144 x 2048: 9.30 vs 9.93 us).
+        if (by_cost && p.m_blocks == 2 && p.n_blocks == 4)
+            p.waves = 8;
         while (p.waves > 4 && ksteps < 2 * p.waves)
             p.waves /= 2;
         const uint32_t tiles = div_up(nb16, nbw) * m_tiles;

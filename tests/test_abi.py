@@ -181,9 +181,16 @@ def test_large_m_plans_tile_kernel():
                       waves=4)
     assert p3.lds_bytes == 3 * 128 * 256 + 3 * 128 * 128 + 256
     # a split may not exceed 64 K steps (one scale per lane)
+    p = w8.plan(200, 256, 128 * 200)
+    assert p.kernel == w8.KERNEL_TILE and p.steps_per_split <= 64
+    _covers(p, 200, 256, 128 * 200)
+    # up to 128 rows over a weight of at most 16 MiB stream when one round
+    # of stream tiles covers C; two rounds go to the tile kernel
     p = w8.plan(100, 256, 128 * 200)
-    assert p.steps_per_split <= 64
-    _covers(p, 100, 256, 128 * 200)
+    assert p.kernel == w8.KERNEL_STREAM and p.m_tiles * p.n_tiles <= 256
+    assert (w8.plan(128, 4096, 4096).kernel, w8.plan(128, 6144, 2048).kernel,
+            w8.plan(129, 4096, 4096).kernel) == (w8.KERNEL_STREAM, w8.KERNEL_TILE,
+                                                 w8.KERNEL_TILE)
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(100, 256, 128 * 200, w8.KERNEL_TILE, 8, 8, 1, depth=3, waves=4)
     with pytest.raises(w8.W8A16Error):
@@ -217,12 +224,12 @@ def test_64_row_tiles():
 
 
 def test_tile_plans_fill_the_cus_with_long_splits():
-    # 128-column tiles would need 4 splits of 8 K steps; 64-column tiles
-    # fill the chip with 2 splits of 16 steps
-    p = w8.plan(96, 4096, 4096)
+    # 128-column tiles would need 4 splits of 12 K steps; 64-column tiles
+    # fill the chip with 2 splits of 24 steps
+    p = w8.plan(96, 4096, 6144)
     assert (p.kernel, p.m_blocks, p.n_blocks, p.splits, p.steps_per_split, p.grid) == \
-        (w8.KERNEL_TILE, 4, 4, 2, 16, 256)
-    _covers(p, 96, 4096, 4096)
+        (w8.KERNEL_TILE, 4, 4, 2, 24, 256)
+    _covers(p, 96, 4096, 6144)
     # 128-column tiles with 16-step splits
     p = w8.plan(48, 8192, 8192)
     assert (p.kernel, p.m_blocks, p.n_blocks, p.splits, p.grid) == (w8.KERNEL_TILE, 4, 8, 4, 256)
@@ -240,12 +247,18 @@ def test_tile_plans_fill_the_cus_with_long_splits():
     (24, 4096, 4096, 1, 2),     # 256 tiles of 16 x 32: 64 vs 80 for 32 x 16
     (17, 2048, 2048, 1, 1),     # 256 tiles of 16 x 16
     (16, 6144, 2048, 1, 2),     # 16 rows: unchanged
+    (48, 4096, 4096, 2, 2),     # two 32 x 32 row tiles: 96 vs 144 for 64 x 16
+    (64, 4096, 4096, 2, 2),
+    (40, 6144, 2048, 2, 4),     # two 32 x 64 row tiles: 128 vs 160 for 64 x 32
+    (48, 2048, 4096, 1, 2),     # three 16 x 32 row tiles: 64 vs 144
 ])
-def test_stream_tile_cost_model_17_to_32_rows(m, n, k, mb, nb):
+def test_stream_tile_cost_model_17_to_64_rows(m, n, k, mb, nb):
     p = w8.plan(m, n, k)
     _covers(p, m, n, k)
     assert (p.kernel, p.m_blocks, p.n_blocks) == (w8.KERNEL_STREAM, mb, nb)
     assert p.m_tiles == -(-m // (16 * mb))
+    if (mb, nb) == (2, 4):
+        assert p.waves == 8
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():

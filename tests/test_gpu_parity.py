@@ -353,12 +353,15 @@ def test_m_sweep(w8):
 
 @pytest.mark.parametrize("m,n,k", [(96, 4096, 4096), (192, 2048, 8192), (24, 8192, 8192),
                                    (48, 4096, 4096), (48, 8192, 8192), (40, 6144, 4096),
-                                   (8, 12288, 5120), (65, 8192, 8192)])
+                                   (8, 12288, 5120), (65, 8192, 8192), (40, 6144, 2048),
+                                   (48, 2048, 4096), (128, 4096, 4096), (96, 2048, 4096),
+                                   (96, 4096, 6144)])
 def test_default_plans_at_size_sampled(w8, m, n, k):
-    """Default plans of the M sweep's larger shapes (64-column tiles, two row
-    tiles, ring with two row blocks, stream with four, one 64-row tile for
+    """Default plans of the M sweep's larger shapes (three or four 32 x 64
+    stream row tiles up to 128 rows over small weights, two 128-row tiles,
+    ring with two row blocks, two 32-row stream tiles, one 64-row tile for
     33..64 rows over a large weight, two for 65 rows, 48-column stream
-    tiles), sampled parity."""
+    tiles, 64-column tiles with 2 splits), sampled parity."""
     p = datagen.make_problem(m, n, k, seed=m + n + k, c_extra_rows=1)
     g = run_gpu(w8, p)
     rows, cols = datagen.sample_indices(m, n, 300, seed=5)
