@@ -415,6 +415,19 @@ def test_w8a8_rejects_before_any_gpu_call():
     assert "W8A8" in w8.last_error()
 
 
+@pytest.mark.parametrize("m,n,k,mb,nb", [
+    (48, 4096, 4096, 2, 2),     # two 32 x 32 row tiles: 64 units per CU vs 80
+    (32, 6144, 2048, 1, 3),     # tie with 32 x 32 (64): fewer rows win
+    (40, 6144, 2048, 2, 4),     # tie with 64 x 32 (96): fewer rows win
+    (24, 4096, 4096, 1, 2),
+    (16, 12288, 5120, 1, 3),    # 16 rows: the fill rule
+])
+def test_w8a8_tile_cost_model(m, n, k, mb, nb):
+    p = w8.plan_w8a8(m, n, k)
+    _covers(p, m, n, k)
+    assert (p.kernel, p.m_blocks, p.n_blocks) == (w8.KERNEL_W8A8, mb, nb)
+
+
 def test_w8a8_plans():
     p = w8.plan_w8a8(8, 4096, 4096)
     assert (p.kernel, p.splits, p.depth, p.m_blocks) == (w8.KERNEL_W8A8, 1, 2, 1)

@@ -622,7 +622,8 @@ def test_w8a8_exact_data_every_variant(w8, mb, nb, waves, m):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 256), (8, 4096, 4096), (16, 12288, 5120),
-                                   (32, 6144, 2048), (100, 700, 1280)])
+                                   (32, 6144, 2048), (100, 700, 1280), (48, 4096, 4096),
+                                   (40, 6144, 2048), (24, 4096, 4096)])
 def test_w8a8_default_plan_within_tolerance(w8, m, n, k):
     """Random codes and log-uniform scales, default plan, sampled against
     the oracle with the W8A16 tolerance form."""
