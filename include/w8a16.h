@@ -25,8 +25,11 @@
  * the call.  The library keeps no pointer to them.  It owns one split-K
  * workspace and counter array per (device, stream), allocated with
  * hipMalloc on first use and grown when a larger plan needs it (growing
- * first waits for the stream); make one call on a stream before capturing
- * that stream into a HIP graph.
+ * first waits for the stream).  The first call on a device whose plan
+ * splits K also runs a short dispatch probe (a 4096-workgroup grid that
+ * records each workgroup's XCD) on `stream` and waits for it, once per
+ * device.  Make one call with the largest plan on a stream before
+ * capturing that stream into a HIP graph.
  *
  * Alignment and aliasing: A, W, S and C must be 16-byte aligned (torch
  * allocations are).  C must not overlap A, W or S.  c_row_stride may be any
