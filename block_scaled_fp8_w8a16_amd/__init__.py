@@ -39,6 +39,7 @@ KERNEL_W8A8 = 4
 FLAG_DIRECT = 1
 FLAG_A8 = 2
 FLAG_XCD_LOCAL = 4
+FLAG_XCD_TEST_MIXED = 8
 
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",

@@ -173,7 +173,7 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
     }
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
-    g.xcd_local = xcd_local ? 1u : 0u;
+    g.xcd_local = !xcd_local ? 0u : (plan.flags & W8A16_FLAG_XCD_TEST_MIXED) ? 2u : 1u;
     g.a = static_cast<const uint8_t *>(a);
     g.w = static_cast<const uint8_t *>(w_fp8);
     g.scale = block_scale;

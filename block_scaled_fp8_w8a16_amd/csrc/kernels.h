@@ -23,7 +23,8 @@ struct GemmArgs {
     uint32_t *counters;     // split-K arrival counters, zero between calls
     uint32_t a_stride, c_stride, m, n, k;
     uint32_t m_tiles, n_tiles, splits, steps_per_split;
-    uint32_t xcd_local;     // splits of a tile share one XCD's L2 (W8A16_FLAG_XCD_LOCAL)
+    uint32_t xcd_local;     // splits of a tile share one XCD's L2 (W8A16_FLAG_XCD_LOCAL);
+                            // 2: odd splits publish as if off their XCD (validation)
 };
 
 // Up to W8A16_MAX_BATCH GEMMs in one grid of the stream kernel: problem i

@@ -161,7 +161,9 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             snprintf(buf, sizeof buf, "w8a16_plan: depth=%u must be 1, 2 or 4", p->depth);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->flags & ~(uint32_t)(W8A16_FLAG_DIRECT | W8A16_FLAG_XCD_LOCAL)) {
+        if (p->flags & ~(uint32_t)(W8A16_FLAG_DIRECT | W8A16_FLAG_XCD_LOCAL |
+                                   W8A16_FLAG_XCD_TEST_MIXED) ||
+            ((p->flags & W8A16_FLAG_XCD_TEST_MIXED) && !(p->flags & W8A16_FLAG_XCD_LOCAL))) {
             snprintf(buf, sizeof buf, "w8a16_plan: unknown flags 0x%x", p->flags);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }

@@ -328,7 +328,8 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     // finds itself on another XCD than round-robin dispatch puts it (read
     // from the hardware register) publishes with the device-scope release,
     // and its arrival is marked so that the last split acquires too.
-    const bool foreign = g.xcd_local && xcc_id() != (blockIdx.x & 7u);
+    const bool foreign = g.xcd_local && (xcc_id() != (blockIdx.x & 7u) ||
+                                         (g.xcd_local == 2u && (split & 1u)));
     const bool local = g.xcd_local && !foreign;
     f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES)

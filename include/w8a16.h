@@ -132,7 +132,11 @@ enum {
      * of 8 with a whole number of tiles' splits per XCD; the library checks
      * once per device that workgroups are dispatched round-robin over the
      * XCDs and uses the device-scope path where they are not. */
-    W8A16_FLAG_XCD_LOCAL = 4u
+    W8A16_FLAG_XCD_LOCAL = 4u,
+    /* Validation of W8A16_FLAG_XCD_LOCAL (tests only): the workgroups of
+     * odd-numbered splits publish as if they ran off their XCD (device-scope
+     * release, marked arrival), so the mixed path runs on any device. */
+    W8A16_FLAG_XCD_TEST_MIXED = 8u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

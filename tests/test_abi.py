@@ -304,6 +304,13 @@ def test_xcd_local_plans_need_whole_tiles_per_xcd():
             w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, sp, depth=1,
                          flags=w8.FLAG_XCD_LOCAL, waves=8)
         assert e.value.status == w8.ERR_BAD_PLAN and "XCD" in str(e.value)
+    # the mixed-publication validation flag only with XCD-local splits
+    p = w8.make_plan(32, 768, 2048, w8.KERNEL_STREAM, 2, 1, 2, depth=1,
+                     flags=w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED, waves=8)
+    assert p.flags == w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(32, 768, 2048, w8.KERNEL_STREAM, 2, 1, 2, depth=1,
+                     flags=w8.FLAG_XCD_TEST_MIXED, waves=8)
     # other kernels take no XCD-local flag
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 4, 8, 2, depth=4,

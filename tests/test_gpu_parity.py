@@ -197,6 +197,23 @@ def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
     check_full(p2, g2, exact=True)
 
 
+@pytest.mark.parametrize("mb,nb", [(1, 1), (1, 4), (2, 2), (4, 1)])
+@pytest.mark.parametrize("splits,ksteps", [(2, 16), (3, 13), (8, 64)])
+def test_exact_data_xcd_mixed_publication(w8, mb, nb, splits, ksteps):
+    """Odd splits publish as if off their XCD (device-scope release, marked
+    arrival) while even ones publish through the L2: the marks must send the
+    last split to the device-scope reads, whichever split it is."""
+    m, n, k = 16 * mb - 1, 16 * nb * 8 - 3, 128 * ksteps
+    p1 = exact_problem(m, n, k, seed=8100 + 100 * mb + 10 * nb + splits)
+    p2 = exact_problem(m, n, k, seed=8200 + 100 * mb + 10 * nb + splits)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1,
+                        flags=w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED, waves=4)
+    assert plan.grid == 8 * plan.splits
+    g1, g2 = run_gpu_pair(w8, p1, p2, plan, torch.cuda.Stream())
+    check_full(p1, g1, exact=True)
+    check_full(p2, g2, exact=True)
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 8192), (16, 1024, 8192), (4, 2048, 14336),
                                    (8, 512, 8192), (16, 1536, 5120), (32, 768, 2048),
                                    (1, 128, 65536)])
