@@ -92,6 +92,10 @@ __device__ __forceinline__ f32x4_t load_l2(const f32x4_t *p)
     return v;
 }
 
+// Cache-policy operand of the global_load_lds builtin for the non-temporal
+// hint (the `nt` bit on gfx950).
+constexpr int kNonTemporal = 2;
+
 // LDS pointer type of the global_load_lds builtin (LDS DMA).
 typedef __attribute__((address_space(3))) void lds_void_t;
 

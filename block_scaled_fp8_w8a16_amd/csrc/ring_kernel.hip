@@ -66,18 +66,24 @@ struct RingShape {
 };
 
 // Issue this wave's NI loads of physical stage `ps` into ring slot `dst`.
-// Lanes whose K step lies past K read their clamped stage-0 address.
+// Lanes whose K step lies past K read their clamped stage-0 address.  Bit u
+// of the wave-uniform `wmask` marks load u as a weight load: the weight is
+// read once (the ring kernel's plans have one row tile), so it carries the
+// non-temporal hint; A, read by every workgroup, does not.
 template <int NI>
 __device__ __forceinline__ void ring_issue(uint8_t *dst, uint32_t ps, uint32_t sk,
                                            uint32_t ksteps, const uint8_t *const *src,
                                            const uint32_t *stride, const uint32_t *lstep,
-                                           const uint32_t *ldso)
+                                           const uint32_t *ldso, uint32_t wmask)
 {
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const bool ok = ps * sk + lstep[u] < ksteps;
         const uint8_t *a = src[u] + (ok ? ps * stride[u] : 0u);
-        __builtin_amdgcn_global_load_lds(a, (lds_void_t *)(dst + ldso[u]), 16, 0, 0);
+        if ((wmask >> u) & 1u)
+            __builtin_amdgcn_global_load_lds(a, (lds_void_t *)(dst + ldso[u]), 16, 0, kNonTemporal);
+        else
+            __builtin_amdgcn_global_load_lds(a, (lds_void_t *)(dst + ldso[u]), 16, 0, 0);
     }
 }
 
@@ -115,10 +121,12 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_ring_kernel(GemmArgs g)
     // ---- DMA sources of this wave's loads (load i = wave + WAVES * u) ----
     const uint8_t *src[S::NI];
     uint32_t stride[S::NI], lstep[S::NI], ldso[S::NI];
+    uint32_t wmask = 0;
 #pragma unroll
     for (int u = 0; u < S::NI; ++u) {
         const uint32_t i = wave + WAVES * u;
         if (i < (uint32_t)S::NWI) {
+            wmask |= 1u << u;
             // 8 / SK weight rows per load, SK * 8 chunks (lanes) per row
             constexpr uint32_t LPR = SK * 8;
             const uint32_t r = i * (8 / SK) + lane / LPR;
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_ring_kernel(GemmArgs g)
     // latency, bounds the start.)
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
-        ring_issue<S::NI>(lds + s * S::STAGE, phys(s), SK, ksteps, src, stride, lstep, ldso);
+        ring_issue<S::NI>(lds + s * S::STAGE, phys(s), SK, ksteps, src, stride, lstep, ldso, wmask);
 
     uint32_t slot = 0;
     for (uint32_t st = 0; st < nst; ++st) {
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_ring_kernel(GemmArgs g)
         if (st + NST - 1 < nst) {
             const uint32_t fill = slot == 0 ? NST - 1 : slot - 1;
             ring_issue<S::NI>(lds + fill * S::STAGE, phys(st + NST - 1), SK, ksteps, src, stride,
-                              lstep, ldso);
+                              lstep, ldso, wmask);
         }
 
         // The WK waves of column block jb take its logical steps
