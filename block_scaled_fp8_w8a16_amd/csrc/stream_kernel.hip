@@ -379,14 +379,12 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
 // row tile (measured on MI355X, us per call: 8 x 4096 x 4096 6.00 -> 5.75,
 // 16 x 12288 x 5120 15.0 -> 14.2, 1 x 1024 x 8192 5.58 -> 5.18; with two
 // row tiles it cost 1-2 %: 32 x 6144 x 2048 6.80 -> 6.89).
-template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES>
+// One instance per weight load form, chosen on the host (the batched grid,
+// whose arms differ, chooses per arm in the kernel).
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES, bool NTW>
 __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_kernel(GemmArgs g)
 {
-    const uint32_t lid = logical_wg(blockIdx.x, gridDim.x);
-    if (g.m_tiles == 1)
-        stream_tile<MB, NBW, DEPTH, DIRECT, WAVES, true>(g, lid);
-    else
-        stream_tile<MB, NBW, DEPTH, DIRECT, WAVES, false>(g, lid);
+    stream_tile<MB, NBW, DEPTH, DIRECT, WAVES, NTW>(g, logical_wg(blockIdx.x, gridDim.x));
 }
 
 // Several independent GEMMs in one grid: problem i owns logical workgroups
@@ -410,15 +408,15 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_stream_batched_kernel(BatchA
         stream_tile<MB, NBW, DEPTH, DIRECT, WAVES, false>(g, lid - base);
 }
 
-template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES, typename Args>
-hipError_t launch_stream_t(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES, bool NTW, typename Args>
+hipError_t launch_stream_k(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     constexpr bool batched = std::is_same<Args, BatchArgs>::value;
     void (*kern)(Args);
     if constexpr (batched)
         kern = w8a16_stream_batched_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
     else
-        kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES>;
+        kern = w8a16_stream_kernel<MB, NBW, DEPTH, DIRECT, WAVES, NTW>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes, kMaxLdsBytes,
                              lds_set);
@@ -426,6 +424,17 @@ hipError_t launch_stream_t(const Args &g, const w8a16_plan_t &p, hipStream_t str
         return e;
     hipLaunchKernelGGL(kern, dim3(p.grid), dim3(p.block), p.lds_bytes, stream, g);
     return hipGetLastError();
+}
+
+template <int MB, int NBW, int DEPTH, bool DIRECT, int WAVES, typename Args>
+hipError_t launch_stream_t(const Args &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    if constexpr (std::is_same<Args, BatchArgs>::value)
+        return launch_stream_k<MB, NBW, DEPTH, DIRECT, WAVES, false>(g, p, stream);
+    else if (g.m_tiles == 1)
+        return launch_stream_k<MB, NBW, DEPTH, DIRECT, WAVES, true>(g, p, stream);
+    else
+        return launch_stream_k<MB, NBW, DEPTH, DIRECT, WAVES, false>(g, p, stream);
 }
 
 template <int MB, int NBW, int DEPTH, bool DIRECT, typename Args>
