@@ -398,9 +398,9 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         // best plans give each CU about one workgroup tile, enough waves
         // that every wave has only a few K steps (so a CU's whole share of
         // the weight is requested in about one memory round trip), and no K
-        // split across workgroups: the agent-scope release that publishing a
-        // split partial needs writes back the L2 and costs far more than it
-        // saves.
+        // split while the tiles fill the CUs: the last split's tail (its
+        // partial reads) costs more than the A bytes a split saves.  Narrow
+        // N splits K (below).
         p.kernel = W8A16_KERNEL_STREAM;
         p.depth = 1;
         p.flags = 0;
@@ -429,9 +429,10 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         if (stream_shape_supported(p.m_blocks, 3) && nbw > 1 &&
             occupancy(3) > occupancy(nbw) + 0.1)
             nbw = 3;
-        // 17..64 rows: a CU's time goes with the bytes it requests (A rows
-        // plus weight rows of its tiles, times its rounds of tiles), so
-        // take the 16-, 32- or 64-row tile that needs the fewest.  Measured
+        // Above 16 rows (up to 64, or 128 over a weight of at most 16 MiB):
+        // a CU's time goes with the bytes it requests (A rows plus weight
+        // rows of its tiles, times its rounds of tiles), so take the 16-,
+        // 32- or 64-row tile that needs the fewest.  Measured
         // on MI355X (us per call, old tile -> chosen tile): 32 x 6144 x 2048
         // 32 x 32 7.43 -> two 16 x 48 7.06; 48 x 4096 x 4096 64 x 16 12.19
         // -> two 32 x 32 9.95; 40 x 6144 x 2048 64 x 32 10.12 -> two 32 x 64

@@ -9,11 +9,11 @@
 // the kernel is organised around streaming W once with 16-byte coalesced
 // loads:
 //
-//   * A workgroup (4 waves) owns NBW 16-column blocks of C (16 weight rows
-//     each) and MB 16-row blocks of C, over a range of 128-wide K steps.
-//     Its 4 waves take interleaved K steps (wave w: steps s0+w, s0+w+4, ...),
-//     so at any time the 4 waves read 4 adjacent 128-byte pieces of each
-//     weight row.
+//   * A workgroup (W = 4, 8 or 16 waves) owns NBW 16-column blocks of C
+//     (16 weight rows each) and MB 16-row blocks of C, over a range of
+//     128-wide K steps.  Its waves take interleaved K steps (wave w: steps
+//     s0+w, s0+w+W, ...), so at any time the W waves read W adjacent
+//     128-byte pieces of each weight row.
 //   * Per K step a wave loads its weight rows (8 lanes per 128-byte row
 //     segment) and the A rows (16 lanes per 256-byte row segment) into
 //     registers, writes them to its private LDS area in an XOR-swizzled
@@ -36,10 +36,14 @@
 //     step partials in each wave's accumulator changes; the set does not.
 //   * Each step's 16x16 MFMA partial starts from zero and is folded into
 //     the FP32 accumulator as acc = fma(scale, partial, acc).
-//   * The 4 waves' accumulators are added in LDS in wave order.  With K
+//   * The waves' accumulators are added in LDS in wave order.  With K
 //     split across workgroups (splits > 1), each split writes its FP32 tile
 //     to a workspace, and the last workgroup to arrive at the tile's counter
 //     adds the splits in split order, so every run gives the same bits.
+//     The splits of a tile run on one XCD and publish through its L2
+//     without a device-wide release (XCD-local plans).
+//   * A plan with one row tile reads each weight byte once and loads it
+//     with the non-temporal hint.
 //   * Columns and rows past n and m are computed from clamped (valid)
 //     addresses and never stored; A pitch padding is never read.
 
