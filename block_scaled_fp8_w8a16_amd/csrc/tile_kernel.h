@@ -64,14 +64,15 @@ using namespace dev;
 // buffer: loads u = 0..N-1 of the wave's group g, each one 1 KiB of LDS.
 // __device__ functions rather than lambdas: a lambda in a kernel is also
 // compiled for the host, where the DMA builtin does not exist.
-template <int N, uint32_t STEP_BYTES>
+// AUX: cache-policy operand (kNonTemporal for a weight read once).
+template <int N, uint32_t STEP_BYTES, int AUX = 0>
 __device__ __forceinline__ void issue_ring(uint8_t *dst, uint32_t grp, uint32_t t,
                                            const uint8_t *const *src)
 {
 #pragma unroll
     for (int u = 0; u < N; ++u)
         __builtin_amdgcn_global_load_lds(src[u] + t * STEP_BYTES,
-                                         (lds_void_t *)(dst + (grp * N + u) * 1024u), 16, 0, 0);
+                                         (lds_void_t *)(dst + (grp * N + u) * 1024u), 16, 0, AUX);
 }
 
 // Producer-wave forms: the whole ring's loads of one step, each address
@@ -94,7 +95,7 @@ __device__ __forceinline__ void issue_a_all(uint8_t *dst, uint32_t t, const Gemm
     }
 }
 
-template <int N>
+template <int N, int AUX>
 __device__ __forceinline__ void issue_w_all(uint8_t *dst, uint32_t t, const GemmArgs &g,
                                             uint32_t n0, uint32_t lane)
 {
@@ -104,7 +105,7 @@ __device__ __forceinline__ void issue_w_all(uint8_t *dst, uint32_t t, const Gemm
         const uint32_t c = (lane & 7u) ^ wswz(r & 15u);
         const uint32_t row = min(n0 + r, g.n - 1u);
         __builtin_amdgcn_global_load_lds(g.w + (size_t)row * g.k + c * 16u + t * 128u,
-                                         (lds_void_t *)(dst + i * 1024u), 16, 0, 0);
+                                         (lds_void_t *)(dst + i * 1024u), 16, 0, AUX);
     }
 }
 
@@ -122,9 +123,12 @@ __device__ __forceinline__ void wait_vm_ahead(uint32_t ahead)
     }
 }
 
-template <int MT, int NT, int WST, int AST, int KH, bool PROD>
+// NTW: the weight's DMA carries the non-temporal hint (one row tile reads
+// each weight byte once; the host picks the instance).
+template <int MT, int NT, int WST, int AST, int KH, bool PROD, bool NTW>
 __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_kernel(GemmArgs g)
 {
+    constexpr int WAUX = NTW ? kNonTemporal : 0;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr uint32_t kABytes = MT * 256;   // one K step of A in LDS
     constexpr uint32_t kWBytes = NT * 128;
@@ -244,9 +248,9 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
         for (int st = 0; st < WST - 1; ++st)
             if (s0 + st < s1) {
                 if constexpr (PROD)
-                    issue_w_all<NW>(wbuf + st * kWBytes, phys(s0 + st), g, n0, lane);
+                    issue_w_all<NW, WAUX>(wbuf + st * kWBytes, phys(s0 + st), g, n0, lane);
                 else
-                    issue_ring<NW, 128u>(wbuf + st * kWBytes, grp, phys(s0 + st), src);
+                    issue_ring<NW, 128u, WAUX>(wbuf + st * kWBytes, grp, phys(s0 + st), src);
             }
     } else {
         if (scale_wave && s0 < s1) {
@@ -281,9 +285,9 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
                 if (t + WST - 1 < s1) {
                     uint8_t *dst = wbuf + ((idx + WST - 1) % WST) * kWBytes;
                     if constexpr (PROD)
-                        issue_w_all<NW>(dst, phys(t + WST - 1), g, n0, lane);
+                        issue_w_all<NW, WAUX>(dst, phys(t + WST - 1), g, n0, lane);
                     else
-                        issue_ring<NW, 128u>(dst, grp, phys(t + WST - 1), src);
+                        issue_ring<NW, 128u, WAUX>(dst, grp, phys(t + WST - 1), src);
                 }
             } else {
                 if (t + AST - 1 < s1) {
@@ -402,15 +406,15 @@ __global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uin
     store_c4(g, s, row, col);
 }
 
-template <int MT, int NT, int WST, int AST, int KH, bool PROD>
-hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+template <int MT, int NT, int WST, int AST, int KH, bool PROD, bool NTW>
+hipError_t launch_tile_n(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     if constexpr (!tile_variant_ok(MT / 16, NT / 16, WST, AST, 4 * KH + (PROD ? 2 : 0)) ||
                   !tile_depth_built(MT / 16, NT / 16, WST, AST)) {
         (void)g, (void)p, (void)stream;
         return hipErrorInvalidValue;
     } else {
-    auto kern = w8a16_tile_kernel<MT, NT, WST, AST, KH, PROD>;
+    auto kern = w8a16_tile_kernel<MT, NT, WST, AST, KH, PROD, NTW>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), p.lds_bytes, kMaxLdsBytes,
                              lds_set);
@@ -428,6 +432,14 @@ hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
                        ws_rows);
     return hipGetLastError();
     }
+}
+
+template <int MT, int NT, int WST, int AST, int KH, bool PROD>
+hipError_t launch_tile_t(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    if (g.m_tiles == 1)
+        return launch_tile_n<MT, NT, WST, AST, KH, PROD, true>(g, p, stream);
+    return launch_tile_n<MT, NT, WST, AST, KH, PROD, false>(g, p, stream);
 }
 
 template <int MT, int NT, int WST, int AST>
