@@ -197,6 +197,28 @@ def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
     check_full(p2, g2, exact=True)
 
 
+def test_xcd_local_splits_on_concurrent_streams(w8):
+    """Split plans on two streams at once (each stream has its own split
+    workspace and counters): four calls per stream, interleaved, with no
+    synchronisation between them; every result bit-exact."""
+    m, n, k = 13, 16 * 4 * 8 - 3, 128 * 32
+    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, 1, 4, 4, depth=1,
+                        flags=w8.FLAG_XCD_LOCAL, waves=8)
+    assert plan.splits == 4 and plan.grid == 32
+    probs = [exact_problem(m, n, k, seed=8400 + i) for i in range(8)]
+    bufs = [(dev_u16(p.a), dev(p.w), dev(p.scale), dev_u16(p.c)) for p in probs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for i, (p, (a, w, s, c)) in enumerate(zip(probs, bufs)):
+        st = w8.gemm_raw(a.data_ptr(), p.a_row_stride, w.data_ptr(), s.data_ptr(),
+                         c.data_ptr(), p.c_row_stride, m, n, k, streams[i % 2].cuda_stream,
+                         plan)
+        assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    for p, (_, _, _, c) in zip(probs, bufs):
+        check_full(p, c.cpu().numpy().view(np.uint16).reshape(p.c.shape), exact=True)
+
+
 @pytest.mark.parametrize("mb,nb", [(1, 1), (1, 4), (2, 2), (4, 1)])
 @pytest.mark.parametrize("splits,ksteps", [(2, 16), (3, 13), (8, 64)])
 def test_exact_data_xcd_mixed_publication(w8, mb, nb, splits, ksteps):
