@@ -7,6 +7,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import block_scaled_fp8_w8a16_amd as w8
@@ -259,6 +260,35 @@ def test_stream_tile_cost_model_17_to_64_rows(m, n, k, mb, nb):
     assert p.m_tiles == -(-m // (16 * mb))
     if (mb, nb) == (2, 4):
         assert p.waves == 8
+
+
+STREAM_TILES = [(1, 1), (1, 2), (1, 3), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
+
+
+def _stream_cost(m, n, mb, nb, cus=256):
+    """Bytes per 128 of K one CU requests: the tile's BF16 A rows plus FP8
+    weight rows, times its rounds of tiles."""
+    tiles = -(-m // (16 * mb)) * -(-((n + 15) // 16) // nb)
+    return -(-tiles // cus) * (32 * mb + 16 * nb)
+
+
+def test_stream_tile_minimises_bytes_per_cu():
+    """Property of the planner over a sweep of shapes: above 16 rows, a
+    stream plan's tile costs no more than any built stream tile (32 x 128
+    left out), by the bytes-per-CU model."""
+    rng = np.random.default_rng(17)
+    checked = 0
+    for _ in range(400):
+        m = int(rng.integers(17, 129))
+        n = int(rng.integers(1, 12289))
+        k = 128 * int(rng.integers(1, 41))
+        p = w8.plan(m, n, k)
+        if p.kernel != w8.KERNEL_STREAM:
+            continue
+        best = min(_stream_cost(m, n, mb, nb) for mb, nb in STREAM_TILES)
+        assert _stream_cost(m, n, p.m_blocks, p.n_blocks) == best, (m, n, k, p.as_dict())
+        checked += 1
+    assert checked > 200
 
 
 def test_split_k_only_when_tiles_leave_cus_idle():
