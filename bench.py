@@ -658,7 +658,7 @@ def main():
                              "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2),
                              "tflops": result["tflops"],
                              "pct_mfma": round(100 * result["tflops"] / BF16_PEAK_TFLOPS, 2),
-                             "output_sane": sane, "plan": plan.as_dict()})
+                             "output_sane": sane, "plan": plan.as_dict(), "seed": wl.seed})
                 continue
             log("generating %s" % other.name)
             op = datagen.make_workload(other)
@@ -679,7 +679,7 @@ def main():
                          "tflops": round(otf, 3),
                          "pct_mfma": round(100 * otf / BF16_PEAK_TFLOPS, 2),
                          "output_sane": ok, "plan": oplan.as_dict(),
-                         "arena_replicas": orep})
+                         "arena_replicas": orep, "seed": other.seed})
             del op
         result["all_workloads"] = rows
 
