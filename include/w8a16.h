@@ -128,10 +128,14 @@ enum {
     /* Stream kernel with splits > 1: the K splits of a tile publish their
      * FP32 partials through the L2 of the XCD they all run on, with no
      * device-wide release (a device-scope release writes back the whole L2
-     * and costs microseconds over a grid).  Needs the grid to be a multiple
-     * of 8 with a whole number of tiles' splits per XCD; the library checks
+     * and costs microseconds over a grid).  w8a16_plan() sets it on every
+     * plan that splits K.  w8a16_plan_finalize() rejects it
+     * (W8A16_ERR_BAD_PLAN) unless splits >= 2, the grid is a multiple of 8
+     * and each eighth of the grid holds whole tiles.  The library checks
      * once per device that workgroups are dispatched round-robin over the
-     * XCDs and uses the device-scope path where they are not. */
+     * XCDs and uses the device-scope path where they are not.  A stream
+     * plan that splits K without the flag always uses the device-scope
+     * path: correct on any dispatch, much slower. */
     W8A16_FLAG_XCD_LOCAL = 4u,
     /* Validation of W8A16_FLAG_XCD_LOCAL (tests only): the workgroups of
      * odd-numbered splits publish as if they ran off their XCD (device-scope
