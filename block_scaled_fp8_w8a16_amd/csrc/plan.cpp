@@ -690,8 +690,39 @@ int plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_cou
             p.n_blocks = c;
             break;
         }
+    // Above 16 rows, the single-GEMM bytes-per-CU choice over all arms'
+    // tiles: the 16-, 32- or 64-row tile whose rounds of tiles ask each CU
+    // for the fewest A and weight bytes (32 x 128 tiles left out).
+    bool by_cost = false;
+    if (max_m > 16) {
+        const uint32_t keep_mb = p.m_blocks, keep_nb = p.n_blocks;
+        auto cost = [&](uint32_t mb, uint32_t nb) {
+            p.m_blocks = mb;
+            const uint64_t t = tiles_for(nb);
+            return (t + p.cu_count - 1) / p.cu_count * (32ull * mb + 16ull * nb);
+        };
+        uint64_t best = cost(keep_mb, keep_nb);
+        uint32_t bmb = keep_mb, bnb = keep_nb;
+        const uint32_t mbs[3] = {4, 2, 1}, nbs[5] = {8, 4, 3, 2, 1};
+        for (uint32_t mb : mbs)
+            for (uint32_t nb : nbs) {
+                if (!stream_shape_supported(mb, nb) || (mb == 2 && nb == 8))
+                    continue;
+                const uint64_t c = cost(mb, nb);
+                if (c < best) {
+                    best = c;
+                    bmb = mb;
+                    bnb = nb;
+                }
+            }
+        p.m_blocks = bmb;
+        p.n_blocks = bnb;
+        by_cost = true;
+    }
     const uint32_t pairs = p.m_blocks * p.n_blocks;
     p.waves = pairs == 1 ? 16 : (pairs <= 4 ? 8 : 4);
+    if (by_cost && p.m_blocks == 2 && p.n_blocks == 4)
+        p.waves = 8;
     while (p.waves > 4 && min_ksteps < 2 * p.waves)
         p.waves /= 2;
     // Finalize against the tallest, widest, longest problem for the block,

@@ -383,11 +383,17 @@ def test_batched_plan_one_variant_for_all_problems():
     assert p.grid == sum(tiles) and p.n_tiles == sum(tiles) and p.m_tiles == 1
     assert p.grid >= 3 * 256 // 4          # fills about three quarters of the CUs
     assert p.block == 64 * p.waves and p.lds_bytes <= 160 * 1024
-    # the tallest problem sets the row blocks; the shortest K the waves
+    # above 16 rows the tile with the fewest bytes per CU over all arms'
+    # tiles (small arms: 16-row tiles, several per tall arm); the shortest K
+    # sets the waves
     p = w8.plan_batched([(40, 512, 1024), (3, 256, 256)])
-    assert p.m_blocks == 4 and p.m_tiles == 1
+    assert p.m_blocks == 1 and p.m_tiles == 3
     assert p.waves == 4                    # K = 256: two steps
-    assert w8.plan_batched([(17, 64, 128)]).m_blocks == 2
+    assert w8.plan_batched([(17, 64, 128)]).m_blocks == 1
+    # Q/K/V arms of 48 rows: two 32 x 64 row tiles per arm, eight waves
+    p = w8.plan_batched([(48, 4096, 4096), (48, 1024, 4096), (48, 1024, 4096)])
+    assert (p.m_blocks, p.n_blocks, p.m_tiles, p.waves) == (2, 4, 2, 8)
+    assert p.grid == 2 * (64 + 16 + 16)
 
 
 def test_batched_rejections_name_the_descriptor():
