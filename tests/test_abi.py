@@ -396,6 +396,24 @@ def test_batched_plan_one_variant_for_all_problems():
     assert p.grid == 2 * (64 + 16 + 16)
 
 
+def test_batched_tile_minimises_bytes_per_cu():
+    """Property of the batched planner: above 16 rows the variant costs no
+    more, over all arms' tiles, than any built stream tile (32 x 128 left
+    out) by the bytes-per-CU model."""
+    rng = np.random.default_rng(23)
+    for _ in range(200):
+        arms = [(int(rng.integers(1, 65)), int(rng.integers(1, 8193)),
+                 128 * int(rng.integers(2, 41))) for _ in range(int(rng.integers(1, 5)))]
+        if max(m for m, _, _ in arms) <= 16:
+            continue
+        p = w8.plan_batched(arms)
+
+        def cost(mb, nb):
+            tiles = sum(-(-m // (16 * mb)) * -(-((n + 15) // 16) // nb) for m, n, _ in arms)
+            return -(-tiles // 256) * (32 * mb + 16 * nb)
+        assert cost(p.m_blocks, p.n_blocks) == min(cost(mb, nb) for mb, nb in STREAM_TILES), arms
+
+
 def test_batched_rejections_name_the_descriptor():
     with pytest.raises(w8.W8A16Error) as e:
         w8.plan_batched([])
