@@ -219,6 +219,59 @@ def _pmc_values(directory: str, counter: str):
     return vals
 
 
+PIPELINE_GROUPS = (
+    "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_UTCL1_TRANSLATION_MISS_sum",
+    "TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum",
+    "TCP_UTCL1_TRANSLATION_HIT_sum TCP_UTCL1_STALL_MULTI_MISS_sum TCP_TCR_TCP_STALL_CYCLES_sum "
+    "TCP_TCP_TA_DATA_STALL_CYCLES_sum",
+    "TCC_HIT_sum TCC_MISS_sum TCC_TAG_STALL_sum GRBM_GUI_ACTIVE",
+)
+PIPELINE_WORKLOADS = ("m8_n4096_k4096", "m16_n12288_k5120", "m128_n8192_k8192")
+
+
+def summarize_pipeline(root: str):
+    """Writes profiles/memory_pipeline_counters.txt from the rocprofv3 PMC
+    runs ROOT/<workload>_g<i> (counter group i of PIPELINE_GROUPS, each a
+    --traffic-run of the workload): per GEMM kernel, each counter's mean over
+    its dispatches."""
+    import csv
+    import glob
+    lines = ["# L1/L2 pipeline counters per dispatch (cold-weight benchmark calls), rocprofv3 PMC",
+             "# commands (run from /tmp with TMPDIR=/tmp), one run per counter group G and workload W:",
+             "#   rocprofv3 --pmc <G> --output-format csv -d ROOT/<W>_g<i> -- python3 bench.py "
+             "--traffic-run <W> ; python3 bench.py --summarize-pipeline ROOT"]
+    for i, grp in enumerate(PIPELINE_GROUPS):
+        lines.append("# group %d: [%s]" % (i, grp))
+    lines.append("# values are means over the dispatches of the run; *_sum counters are summed over "
+                 "all CUs / L2 channels")
+    lines.append("kernel_source_hash: %s" % kernel_source_hash())
+    for wl in PIPELINE_WORKLOADS:
+        vals = {}
+        for i in range(len(PIPELINE_GROUPS)):
+            d = os.path.join(root, "%s_g%d" % (wl, i))
+            for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                with open(path) as fh:
+                    for r in csv.DictReader(fh):
+                        if "w8a16" not in r["Kernel_Name"]:
+                            continue
+                        name = r["Kernel_Name"].replace("void ", "").replace(
+                            "w8a16::(anonymous namespace)::", "").split("(")[0]
+                        vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                            float(r["Counter_Value"]))
+        lines.append("")
+        lines.append("workload %s" % wl)
+        for kern in sorted(vals):
+            lines.append("  kernel %s" % kern)
+            for cname in sorted(vals[kern]):
+                v = vals[kern][cname]
+                lines.append("    %-36s %.4g" % (cname, sum(v) / len(v)))
+    path = os.path.join(ROOT, "profiles", "memory_pipeline_counters.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
 def summarize_traffic(fetch_dir: str, write_dir: str, wl_name: str, command: str):
     """Writes profiles/traffic_<workload>.txt: HBM bytes per launch of the
     GEMM kernel(s) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
@@ -551,6 +604,9 @@ def main():
                    "python3 bench.py --steps 50 --warmup 5 --no-cpu --only-main --workload %s ; "
                    "python3 bench.py --summarize-trace TRACE_DIR %s" % (wl_name, wl_name))
         summarize_trace(sys.argv[2], wl_name, cmd)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pipeline":
+        summarize_pipeline(sys.argv[2])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-run":
         traffic_run(sys.argv[2] if len(sys.argv) > 2 else MAIN_WORKLOAD)
