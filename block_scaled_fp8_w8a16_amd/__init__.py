@@ -30,6 +30,7 @@ ERR_N_ZERO = 5
 ERR_NULL_PTR = 6
 ERR_BAD_PLAN = 7
 ERR_HIP = 8
+ERR_WORKSPACE = 9
 
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
@@ -39,7 +40,6 @@ KERNEL_W8A8 = 4
 FLAG_DIRECT = 1
 FLAG_A8 = 2
 FLAG_XCD_LOCAL = 4
-FLAG_XCD_TEST_MIXED = 8
 
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",

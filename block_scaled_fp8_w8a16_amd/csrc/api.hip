@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "kernels.h"
 #include "plan.h"
@@ -32,12 +33,13 @@ struct Workspace {
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers replaced by larger ones.  They are never freed: a HIP graph
+// captured with an earlier, smaller plan on that stream keeps their
+// addresses and may still be replayed.
+std::vector<void *> g_retired;
 
 std::mutex g_cu_mutex;
 std::map<int, uint32_t> g_cu_count;
-
-std::mutex g_rr_mutex;
-std::map<int, bool> g_round_robin;
 
 int hip_fail(hipError_t e, const char *what)
 {
@@ -63,75 +65,58 @@ int device_cu_count(int dev, uint32_t *out)
     return W8A16_OK;
 }
 
-// Whether device `dev` dispatches workgroup i to XCD i mod 8 (what the
-// XCD-local split publication relies on), from one probe grid per device
-// run on `stream` and waited for.  A device that does not, or a failed
-// probe, gets the device-scope publication.
-int device_round_robin(int dev, hipStream_t stream, bool *out)
-{
-    std::lock_guard<std::mutex> lock(g_rr_mutex);
-    auto it = g_round_robin.find(dev);
-    if (it != g_round_robin.end()) {
-        *out = it->second;
-        return W8A16_OK;
-    }
-    constexpr uint32_t kProbeGrid = 4096;
-    uint32_t *d = nullptr;
-    hipError_t e = hipMalloc(reinterpret_cast<void **>(&d), kProbeGrid * sizeof(uint32_t));
-    if (e != hipSuccess)
-        return hip_fail(e, "hipMalloc(XCD probe)");
-    static uint32_t h[kProbeGrid];
-    e = launch_xcc_probe(d, kProbeGrid, stream);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(h, d, sizeof h, hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(stream);
-    (void)hipFree(d);
-    if (e != hipSuccess)
-        return hip_fail(e, "XCD dispatch probe");
-    bool ok = true;
-    for (uint32_t i = 0; i < kProbeGrid; ++i)
-        ok = ok && h[i] == (i & 7u);
-    g_round_robin[dev] = ok;
-    *out = ok;
-    return W8A16_OK;
-}
-
-// Workspace for `plan` on (dev, stream), grown if needed.  Growing waits for
-// the stream so that no earlier call still uses the old buffers.
+// Workspace for `plan` on (dev, stream), grown if needed.  Growth allocates
+// new buffers and keeps the old ones alive (calls still in flight, and
+// graphs captured earlier, use them), so it needs no synchronisation.  It
+// cannot happen while the stream is being captured into a graph: that
+// returns W8A16_ERR_WORKSPACE and enqueues nothing.
 int get_workspace(int dev, hipStream_t stream, const w8a16_plan_t &plan, Workspace *out)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
-    hipError_t e;
-    if (plan.workspace_bytes > w.ws_bytes || plan.counter_count > w.counter_count) {
-        e = hipStreamSynchronize(stream);
+    const bool grow_ws = plan.workspace_bytes > w.ws_bytes;
+    const bool grow_ctr = plan.counter_count > w.counter_count;
+    if (grow_ws || grow_ctr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess)
-            return hip_fail(e, "hipStreamSynchronize");
+            return hip_fail(e, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone) {
+            char buf[256];
+            snprintf(buf, sizeof buf,
+                     "w8a16_gemm: this plan needs %llu bytes of split-K workspace and %u "
+                     "counters on a stream being captured, which has %llu and %u; make one "
+                     "call with this plan (or a larger one) on the stream before capturing",
+                     (unsigned long long)plan.workspace_bytes, plan.counter_count,
+                     (unsigned long long)w.ws_bytes, w.counter_count);
+            return fail(W8A16_ERR_WORKSPACE, buf);
+        }
     }
-    if (plan.workspace_bytes > w.ws_bytes) {
-        if (w.ws)
-            (void)hipFree(w.ws);
-        w.ws = nullptr;
-        w.ws_bytes = 0;
-        e = hipMalloc(reinterpret_cast<void **>(&w.ws), plan.workspace_bytes);
+    hipError_t e;
+    if (grow_ws) {
+        float *nws = nullptr;
+        e = hipMalloc(reinterpret_cast<void **>(&nws), plan.workspace_bytes);
         if (e != hipSuccess)
             return hip_fail(e, "hipMalloc(workspace)");
+        if (w.ws)
+            g_retired.push_back(w.ws);
+        w.ws = nws;
         w.ws_bytes = plan.workspace_bytes;
     }
-    if (plan.counter_count > w.counter_count) {
-        if (w.counters)
-            (void)hipFree(w.counters);
-        w.counters = nullptr;
-        w.counter_count = 0;
-        e = hipMalloc(reinterpret_cast<void **>(&w.counters),
-                      (size_t)plan.counter_count * sizeof(uint32_t));
+    if (grow_ctr) {
+        uint32_t *nc = nullptr;
+        const size_t bytes = (size_t)plan.counter_count * sizeof(uint32_t);
+        e = hipMalloc(reinterpret_cast<void **>(&nc), bytes);
         if (e != hipSuccess)
             return hip_fail(e, "hipMalloc(counters)");
-        e = hipMemsetAsync(w.counters, 0, (size_t)plan.counter_count * sizeof(uint32_t),
-                           stream);
-        if (e != hipSuccess)
+        e = hipMemsetAsync(nc, 0, bytes, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(nc);
             return hip_fail(e, "hipMemsetAsync(counters)");
+        }
+        if (w.counters)
+            g_retired.push_back(w.counters);
+        w.counters = nc;
         w.counter_count = plan.counter_count;
     }
     *out = w;
@@ -165,15 +150,8 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
         if (st != W8A16_OK)
             return st;
     }
-    bool xcd_local = false;
-    if (plan.kernel == W8A16_KERNEL_STREAM && (plan.flags & W8A16_FLAG_XCD_LOCAL)) {
-        int st = device_round_robin(dev, stream, &xcd_local);
-        if (st != W8A16_OK)
-            return st;
-    }
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
-    g.xcd_local = !xcd_local ? 0u : (plan.flags & W8A16_FLAG_XCD_TEST_MIXED) ? 2u : 1u;
     g.a = static_cast<const uint8_t *>(a);
     g.w = static_cast<const uint8_t *>(w_fp8);
     g.scale = block_scale;

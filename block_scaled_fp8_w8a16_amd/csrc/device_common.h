@@ -67,19 +67,24 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
     return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Id of the XCD this wave runs on (hardware register XCC_ID, bits 3:0).
-__device__ __forceinline__ uint32_t xcc_id()
+// 16-byte store at agent scope: two 8-byte agent-scope atomic stores, which
+// gfx950 issues with the sc1 bit, writing through this XCD's L2 so that a
+// CU on any XCD can read the data once the store has completed (s_waitcnt
+// vmcnt(0)).  Unlike a release fence, nothing else in the L2 is written back.
+__device__ __forceinline__ void store_agent(f32x4_t *p, f32x4_t v)
 {
-    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11));
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    const uint64_t lo = (uint64_t)__builtin_bit_cast(uint32_t, v.x) |
+                        ((uint64_t)__builtin_bit_cast(uint32_t, v.y) << 32);
+    const uint64_t hi = (uint64_t)__builtin_bit_cast(uint32_t, v.z) |
+                        ((uint64_t)__builtin_bit_cast(uint32_t, v.w) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrival-count increment that marks a split published with the
-// device-scope release (the low 16 bits count arrivals).
-constexpr uint32_t kForeignArrival = 1u << 16;
-
-// 16-byte load that does not hit in this CU's L1 (two device-scope 8-byte
-// loads), for data another CU of the same XCD has just stored to the L2.
-__device__ __forceinline__ f32x4_t load_l2(const f32x4_t *p)
+// 16-byte load at agent scope (two 8-byte agent-scope atomic loads, sc1):
+// misses this CU's L1, so it sees what store_agent() wrote on any XCD.
+__device__ __forceinline__ f32x4_t load_agent(const f32x4_t *p)
 {
     const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
     const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -23,8 +23,6 @@ struct GemmArgs {
     uint32_t *counters;     // split-K arrival counters, zero between calls
     uint32_t a_stride, c_stride, m, n, k;
     uint32_t m_tiles, n_tiles, splits, steps_per_split;
-    uint32_t xcd_local;     // splits of a tile share one XCD's L2 (W8A16_FLAG_XCD_LOCAL);
-                            // 2: odd splits publish as if off their XCD (validation)
 };
 
 // Up to W8A16_MAX_BATCH GEMMs in one grid of the stream kernel: problem i
@@ -68,9 +66,6 @@ inline hipError_t allow_lds(const void *kern, uint32_t bytes, uint32_t limit,
 }
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
-// One workgroup per entry of out[0 .. grid): each writes the id of the XCD
-// it ran on.
-hipError_t launch_xcc_probe(uint32_t *out, uint32_t grid, hipStream_t stream);
 hipError_t launch_act_quant(const QuantArgs &q, hipStream_t stream);
 // W8A8: g.a holds FP8 codes (g.a_stride in bytes), a_scales FP32 [m, k/128].
 hipError_t launch_w8a8(const GemmArgs &g, const float *a_scales, const w8a16_plan_t &p,

@@ -161,9 +161,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
             snprintf(buf, sizeof buf, "w8a16_plan: depth=%u must be 1, 2 or 4", p->depth);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->flags & ~(uint32_t)(W8A16_FLAG_DIRECT | W8A16_FLAG_XCD_LOCAL |
-                                   W8A16_FLAG_XCD_TEST_MIXED) ||
-            ((p->flags & W8A16_FLAG_XCD_TEST_MIXED) && !(p->flags & W8A16_FLAG_XCD_LOCAL))) {
+        if (p->flags & ~(uint32_t)(W8A16_FLAG_DIRECT | W8A16_FLAG_XCD_LOCAL)) {
             snprintf(buf, sizeof buf, "w8a16_plan: unknown flags 0x%x", p->flags);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
@@ -460,11 +458,13 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         while (p.waves > 4 && ksteps < 2 * p.waves)
             p.waves /= 2;
         const uint32_t tiles = div_up(nb16, nbw) * m_tiles;
-        // Split K only when the tiles would leave most CUs idle, and only
-        // with XCD-local publication (the device-scope release of a split
-        // partial measured 40-90 us per call over such grids).  Splits
-        // double while the grid fits the CUs, each split keeps 8 or more K
-        // steps and every XCD's range of the grid holds whole tiles; a
+        // Split K only when the tiles would leave most CUs idle.  Splits
+        // publish their partials with write-through stores, never with a
+        // release fence (a device-scope release of a split partial measured
+        // 40-90 us per call over such grids).  Splits double while the grid
+        // fits the CUs, each split keeps 8 or more K steps and every XCD's
+        // range of the grid holds whole tiles (a tile's splits share one
+        // XCD); a
         // split of 32 or more steps keeps 16 waves, shorter ones take 8
         // (measured on MI355X, us per call: 1 x 1024 x 8192 48.9 -> 5.6,
         // 16 x 1024 x 8192 50.1 -> 6.2, 4 x 2048 x 14336 95.2 -> 8.6,
@@ -534,6 +534,8 @@ const char *status_string(int status)
     case W8A16_ERR_NULL_PTR: return "null pointer argument";
     case W8A16_ERR_BAD_PLAN: return "plan does not fit the problem";
     case W8A16_ERR_HIP: return "HIP runtime error";
+    case W8A16_ERR_WORKSPACE: return "split-K workspace unavailable (growth during capture, "
+                                     "or beyond the no-alloc scratch)";
     default: return "unknown status";
     }
 }

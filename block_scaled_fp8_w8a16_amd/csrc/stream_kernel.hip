@@ -40,8 +40,8 @@
 //     split across workgroups (splits > 1), each split writes its FP32 tile
 //     to a workspace, and the last workgroup to arrive at the tile's counter
 //     adds the splits in split order, so every run gives the same bits.
-//     The splits of a tile run on one XCD and publish through its L2
-//     without a device-wide release (XCD-local plans).
+//     Partials are published with agent-scope (write-through) stores and
+//     read with agent-scope loads, with no L2 writeback.
 //   * A plan with one row tile reads each weight byte once and loads it
 //     with the non-temporal hint.
 //   * Columns and rows past n and m are computed from clamped (valid)
@@ -326,57 +326,43 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     }
 
     // ---- split-K: publish this split's tile, the last arrival adds all ----
-    // Device-scope publication: a release (L2 writeback) before the arrival
-    // count and an acquire after it, so splits may run on any XCD.
-    // XCD-local publication: all splits of the tile run on one XCD (the
-    // logical ids of a tile's splits are consecutive and the host made each
-    // XCD's share of ids a whole number of tiles), so their partials meet in
-    // that XCD's L2; a split only waits until its stores have reached the
-    // L2, and the last one reads them past its own L1.  A workgroup that
-    // finds itself on another XCD than round-robin dispatch puts it (read
-    // from the hardware register) publishes with the device-scope release,
-    // and its arrival is marked so that the last split acquires too.
-    const bool foreign = g.xcd_local && (xcc_id() != (blockIdx.x & 7u) ||
-                                         (g.xcd_local == 2u && (split & 1u)));
-    const bool local = g.xcd_local && !foreign;
+    // Each split stores its FP32 partial tile with agent-scope stores, which
+    // write through its XCD's L2, and waits until they have completed before
+    // its arrival is counted.  The last split to arrive acquires at agent
+    // scope (invalidating stale lines) and reads every split's partial with
+    // agent-scope loads, adding them in split order.  Nothing is written back
+    // from the L2 (a release fence would write back the whole L2, which
+    // measured microseconds per call over a grid), and the result does not
+    // depend on which XCD each split ran on.  The splits of a tile are
+    // consecutive logical workgroups, which the logical id map keeps on one
+    // XCD where the planner could arrange it.
     f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES)
-        ws_tile[((size_t)split * P + pi) * 64 + lane] = sum_waves<WAVES, P>(red, pi, lane);
-    if (local)
-        wait_vm<0>();
-    else
-        __threadfence();
+        store_agent(ws_tile + ((size_t)split * P + pi) * 64 + lane,
+                    sum_waves<WAVES, P>(red, pi, lane));
+    wait_vm<0>();
     __syncthreads();
     __shared__ uint32_t last;
+    uint32_t *counter = g.counters + (size_t)tile * kCounterStride;
     if (threadIdx.x == 0) {
-        const uint32_t add = foreign ? 1u + kForeignArrival : 1u;
-        const uint32_t now = atomicAdd(g.counters + (size_t)tile * kCounterStride, add) + add;
-        last = (now & (kForeignArrival - 1u)) == g.splits ? (now >= kForeignArrival ? 2u : 1u)
-                                                             : 0u;
+        const uint32_t now = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        last = now == g.splits ? 1u : 0u;
     }
     __syncthreads();
     if (!last)
         return;
-    if (!g.xcd_local || last == 2u || foreign) {
-        __threadfence();
-        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
-            f32x4_t s = ws_tile[pi * 64 + lane];
-            for (uint32_t sp = 1; sp < g.splits; ++sp)
-                s += ws_tile[((size_t)sp * P + pi) * 64 + lane];
-            const uint32_t j = pi / MB, b = pi % MB;
-            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
-        }
-    } else {
-        for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
-            f32x4_t s = load_l2(ws_tile + pi * 64 + lane);
-            for (uint32_t sp = 1; sp < g.splits; ++sp)
-                s += load_l2(ws_tile + ((size_t)sp * P + pi) * 64 + lane);
-            const uint32_t j = pi / MB, b = pi % MB;
-            store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
-        }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+        f32x4_t s = load_agent(ws_tile + pi * 64 + lane);
+        for (uint32_t sp = 1; sp < g.splits; ++sp)
+            s += load_agent(ws_tile + ((size_t)sp * P + pi) * 64 + lane);
+        const uint32_t j = pi / MB, b = pi % MB;
+        store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
     }
+    // ready for the next call that uses this workspace
     if (threadIdx.x == 0)
-        atomicExch(g.counters + (size_t)tile * kCounterStride, 0u);   // ready for the next call on this stream
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The weight is streamed with the non-temporal hint when the plan has one
@@ -494,19 +480,7 @@ hipError_t launch_stream_any(const Args &g, const w8a16_plan_t &p, hipStream_t s
     }
 }
 
-__global__ __launch_bounds__(64) void w8a16_xcc_probe_kernel(uint32_t *out)
-{
-    if (threadIdx.x == 0)
-        out[blockIdx.x] = xcc_id();
-}
-
 }  // namespace
-
-hipError_t launch_xcc_probe(uint32_t *out, uint32_t grid, hipStream_t stream)
-{
-    hipLaunchKernelGGL(w8a16_xcc_probe_kernel, dim3(grid), dim3(64), 0, stream, out);
-    return hipGetLastError();
-}
 
 hipError_t launch_stream(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {

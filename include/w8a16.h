@@ -24,12 +24,15 @@
  * by the caller, who keeps the buffers alive until the stream has passed
  * the call.  The library keeps no pointer to them.  It owns one split-K
  * workspace and counter array per (device, stream), allocated with
- * hipMalloc on first use and grown when a larger plan needs it (growing
- * first waits for the stream).  The first call on a device whose plan
- * splits K also runs a short dispatch probe (a 4096-workgroup grid that
- * records each workgroup's XCD) on `stream` and waits for it, once per
- * device.  Make one call with the largest plan on a stream before
- * capturing that stream into a HIP graph.
+ * hipMalloc on first use and grown when a larger plan needs it.  Growing
+ * allocates new buffers and keeps the old ones until the process ends, so
+ * calls in flight and HIP graphs captured earlier on that stream stay
+ * valid; it needs no synchronisation.  Growth cannot happen while the
+ * stream is being captured: such a call returns W8A16_ERR_WORKSPACE and
+ * enqueues nothing, so make one call with the largest plan on a stream
+ * before capturing it.  A graph keeps using the workspace of the stream it
+ * was captured on: two replays of graphs captured on one stream must not
+ * overlap in time.
  *
  * Alignment and aliasing: A, W, S and C must be 16-byte aligned (torch
  * allocations are).  C must not overlap A, W or S.  c_row_stride may be any
@@ -37,8 +40,8 @@
  *
  * Errors: every entry point returns a w8a16_status.  Argument errors are
  * detected before anything is enqueued, in the order of the enum below
- * (codes 1..4 in the order the page checks them; 5..7 are checks the page
- * does not make).  w8a16_last_error() then holds a message for the calling
+ * (codes 1..4 in the order the page checks them; 5..7 and 9 are checks the
+ * page does not make).  w8a16_last_error() then holds a message for the calling
  * thread.  Launches are asynchronous: the call returns once the kernel is
  * enqueued on `stream`; a failed enqueue returns W8A16_ERR_HIP.
  */
@@ -60,7 +63,10 @@ typedef enum w8a16_status {
     W8A16_ERR_N_ZERO = 5,            /* n == 0: empty launch */
     W8A16_ERR_NULL_PTR = 6,          /* a, w_fp8, block_scale or c is null */
     W8A16_ERR_BAD_PLAN = 7,          /* a plan that does not fit the problem */
-    W8A16_ERR_HIP = 8                /* allocation or launch failed in HIP */
+    W8A16_ERR_HIP = 8,               /* allocation or launch failed in HIP */
+    W8A16_ERR_WORKSPACE = 9          /* the plan's split-K workspace cannot be provided:
+                                        it would have to grow during stream capture,
+                                        or it exceeds w8a16_gemm_noalloc's scratch */
 } w8a16_status;
 
 /* Kernel families a plan can name. */
@@ -125,22 +131,18 @@ enum {
     /* Ring kernel, m <= 8 with m_blocks == 1: stage 8 A rows instead of 16
      * (derived by w8a16_plan_finalize from m; callers need not set it). */
     W8A16_FLAG_A8 = 2u,
-    /* Stream kernel with splits > 1: the K splits of a tile publish their
-     * FP32 partials through the L2 of the XCD they all run on, with no
-     * device-wide release (a device-scope release writes back the whole L2
-     * and costs microseconds over a grid).  w8a16_plan() sets it on every
-     * plan that splits K.  w8a16_plan_finalize() rejects it
-     * (W8A16_ERR_BAD_PLAN) unless splits >= 2, the grid is a multiple of 8
-     * and each eighth of the grid holds whole tiles.  The library checks
-     * once per device that workgroups are dispatched round-robin over the
-     * XCDs and uses the device-scope path where they are not.  A stream
-     * plan that splits K without the flag always uses the device-scope
-     * path: correct on any dispatch, much slower. */
-    W8A16_FLAG_XCD_LOCAL = 4u,
-    /* Validation of W8A16_FLAG_XCD_LOCAL (tests only): the workgroups of
-     * odd-numbered splits publish as if they ran off their XCD (device-scope
-     * release, marked arrival), so the mixed path runs on any device. */
-    W8A16_FLAG_XCD_TEST_MIXED = 8u
+    /* Stream kernel with splits > 1: the K splits of every tile run on one
+     * XCD (consecutive logical workgroups inside one XCD's contiguous range
+     * of the grid), so the partials they exchange stay in that XCD's L2.
+     * w8a16_plan() sets it on every plan that splits K.
+     * w8a16_plan_finalize() rejects it (W8A16_ERR_BAD_PLAN) unless
+     * splits >= 2, the grid is a multiple of 8 and each eighth of the grid
+     * holds whole tiles.  The publication itself is the same with or
+     * without the flag: each split stores its partial with agent-scope
+     * (write-through) stores, waits for them, then counts its arrival; the
+     * last one acquires at agent scope and reads the partials with
+     * agent-scope loads.  It is correct on whichever XCDs the splits run. */
+    W8A16_FLAG_XCD_LOCAL = 4u
 };
 
 /* Validate the scalar arguments alone, in the documented order.  Pure: no

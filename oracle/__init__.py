@@ -21,9 +21,13 @@ arithmetic reading stated at their functions.
 This module is argument marshalling around that C code, plus the parity
 tolerance the GPU result is graded with.
 
-Parity pins: every function here is pinned by ``tests/test_oracle.py``
-(closed-form and library witnesses for the decodes and the rounding, brute
-force with exact rationals for the GEMM, and invariants).
+Parity pins: every function here is pinned by ``tests/test_oracle.py``:
+closed-form and library witnesses for the decodes and the rounding, brute
+force with exact rationals for the GEMMs, invariants, and for the parity
+tolerance helpers (``bf16_bits_to_f64``, ``bf16_ulp``, ``within_tolerance``)
+torch's BF16 decoding of all 65536 patterns, the gap between consecutive
+BF16 values, and hand-built values exactly at and one BF16 step past the
+bar, for both signs, at zero and for NaN / Inf.
 """
 
 from __future__ import annotations
@@ -298,15 +302,20 @@ def gemm_w8a8_at(qa: np.ndarray, sa: np.ndarray, w: np.ndarray, sw: np.ndarray, 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact BF16 bits -> float64 (vectorised form of bf16_value)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """BF16 spacing at each value: 2^(max(floor(log2|v|), -126) - 7), 2^-133
+    at zero, NaN where v is not finite."""
     v = np.abs(np.asarray(v, dtype=np.float64))
+    fin = np.isfinite(v)
+    v = np.where(fin, v, 1.0)
     with np.errstate(divide="ignore"):
         e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
     e = np.where(v > 0, np.maximum(e, -126.0), -126.0)
-    return np.ldexp(1.0, (e - 7).astype(np.int64))
+    return np.where(fin, np.ldexp(1.0, (e - 7).astype(np.int64)), np.nan)
 
 
 def within_tolerance(gpu_bits: np.ndarray, oracle_bits: np.ndarray,
@@ -315,5 +324,6 @@ def within_tolerance(gpu_bits: np.ndarray, oracle_bits: np.ndarray,
     g = bf16_bits_to_f64(gpu_bits)
     o = bf16_bits_to_f64(oracle_bits)
     lim = np.ldexp(np.asarray(bound, dtype=np.float64), -8) + bf16_ulp(o)
-    ok = np.isfinite(g) & (np.abs(g - o) <= lim)
+    with np.errstate(invalid="ignore"):
+        ok = np.isfinite(g) & (np.abs(g - o) <= lim)
     return ok

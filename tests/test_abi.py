@@ -295,7 +295,7 @@ def test_split_k_only_when_tiles_leave_cus_idle():
     p = w8.plan(1, 128, 65536)
     assert p.splits > 1 and p.grid <= 256
     _covers(p, 1, 128, 65536)
-    # splits always publish XCD-locally: 8 equal ranges of whole tiles
+    # default splits are grouped per XCD: 8 equal ranges of whole tiles
     assert p.flags & w8.FLAG_XCD_LOCAL
     assert p.grid % 8 == 0 and (p.grid // 8) % p.splits == 0
     # tiles that fill the CUs are not split
@@ -334,14 +334,16 @@ def test_xcd_local_plans_need_whole_tiles_per_xcd():
             w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, sp, depth=1,
                          flags=w8.FLAG_XCD_LOCAL, waves=8)
         assert e.value.status == w8.ERR_BAD_PLAN and "XCD" in str(e.value)
-    # the mixed-publication validation flag only with XCD-local splits
-    p = w8.make_plan(32, 768, 2048, w8.KERNEL_STREAM, 2, 1, 2, depth=1,
-                     flags=w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED, waves=8)
-    assert p.flags == w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED
+    # without the flag any split count is a valid stream plan (the splits of
+    # a tile may then run on several XCDs)
+    for m, n, k, mb, nb, sp in bad[1:]:
+        p = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, sp, depth=1, waves=8)
+        assert p.splits == sp and p.flags == 0
+    # an unknown flag bit is rejected
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(32, 768, 2048, w8.KERNEL_STREAM, 2, 1, 2, depth=1,
-                     flags=w8.FLAG_XCD_TEST_MIXED, waves=8)
-    # other kernels take no XCD-local flag
+                     flags=w8.FLAG_XCD_LOCAL | 8, waves=8)
+    # other kernels take no XCD grouping flag
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 4, 8, 2, depth=4,
                      flags=w8.FLAG_XCD_LOCAL, waves=8)

@@ -71,18 +71,29 @@ def check_full(prob, gpu_c, exact=False):
     return oc, bound
 
 
+# Largest weight code magnitude (exclusive) of exact_problem: exponent field
+# e <= 8 (values up to 3.75) for K <= 1024, e <= 5 (up to 0.46875) above.
+def _exact_code_top(k):
+    return 0x48 if k <= 1024 else 0x30
+
+
 def exact_problem(m, n, k, seed, a_row_stride=None, c_row_stride=None, c_extra_rows=1):
     """Operands whose products and FP32 sums are exact: A in {-2..2}, weight
     codes with |value| < 4 for K <= 1024 and < 1/2 for K <= 8192 (all
-    subnormals included), scales in {1/2, 1, 2} -- every product is a
-    multiple of 2^-10 and every partial sum stays below 2^24 such units."""
+    subnormals included), scales in {1/2, 1, 2}.  Every product a*w is a
+    multiple of 2^-9 and every scaled one a multiple of 2^-10; the largest
+    possible |sum| over all of K, 2 * wmax * 2 * K, stays below 2^14, i.e.
+    below 2^24 units of 2^-10, so every FP32 partial sum, in any order and
+    with any split, is exact (asserted below)."""
     assert k <= 8192
+    top = _exact_code_top(k)
+    wmax = max(abs(oracle.e4m3_value(c)) for c in range(top))
+    assert 2.0 * wmax * 2.0 * k < 2.0 ** 14, "exact_problem bound does not hold"
     rng = np.random.default_rng(seed)
     p = datagen.make_problem(m, n, k, seed, a_row_stride, c_row_stride,
                              c_extra_rows=c_extra_rows)
     a_int = rng.integers(-2, 3, size=(m, k)).astype(np.float32)
     p.a[:, :k] = datagen.to_bf16_bits(a_int)
-    top = 0x50 if k <= 1024 else 0x30                             # e <= 9 or e <= 5
     mag = rng.integers(0, top, size=(n, k), dtype=np.uint8)
     sign = rng.integers(0, 2, size=(n, k), dtype=np.uint8) << 7
     p.w[...] = mag | sign
@@ -178,10 +189,10 @@ XCD_SHAPES = STREAM_SHAPES + [(2, 8)]
 @pytest.mark.parametrize("splits,ksteps", [(2, 16), (4, 13), (8, 64)])
 @pytest.mark.parametrize("waves", [4, 8, 16])
 def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
-    """XCD-local split publication: 8 tiles (one per XCD range), two
+    """Split plans grouped per XCD: 8 tiles (one per XCD range), two
     different problems back to back on one stream, so a partial read
-    before its writer's stores reached the L2 (or a stale one from the
-    previous call) breaks bit exactness."""
+    before its writer's stores completed (or a stale one from the previous
+    call) breaks bit exactness."""
     m, n, k = 16 * mb - 3, 16 * nb * 8 - 5, 128 * ksteps
     p1 = exact_problem(m, n, k, seed=7000 + 100 * mb + 10 * nb + splits + waves)
     p2 = exact_problem(m, n, k, seed=9000 + 100 * mb + 10 * nb + splits + waves)
@@ -220,17 +231,19 @@ def test_xcd_local_splits_on_concurrent_streams(w8):
 
 
 @pytest.mark.parametrize("mb,nb", [(1, 1), (1, 4), (2, 2), (4, 1)])
-@pytest.mark.parametrize("splits,ksteps", [(2, 16), (3, 13), (8, 64)])
-def test_exact_data_xcd_mixed_publication(w8, mb, nb, splits, ksteps):
-    """Odd splits publish as if off their XCD (device-scope release, marked
-    arrival) while even ones publish through the L2: the marks must send the
-    last split to the device-scope reads, whichever split it is."""
-    m, n, k = 16 * mb - 1, 16 * nb * 8 - 3, 128 * ksteps
-    p1 = exact_problem(m, n, k, seed=8100 + 100 * mb + 10 * nb + splits)
-    p2 = exact_problem(m, n, k, seed=8200 + 100 * mb + 10 * nb + splits)
-    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1,
-                        flags=w8.FLAG_XCD_LOCAL | w8.FLAG_XCD_TEST_MIXED, waves=4)
-    assert plan.grid == 8 * plan.splits
+@pytest.mark.parametrize("tiles,splits,ksteps", [(1, 8, 64), (2, 4, 16), (3, 8, 24),
+                                                 (5, 3, 13)])
+def test_exact_data_splits_across_xcds(w8, mb, nb, tiles, splits, ksteps):
+    """Split plans without the XCD grouping: the logical id map spreads a
+    tile's splits over several XCDs (one tile of 8 splits: one split per
+    XCD), so partials cross L2s.  Two different problems back to back on
+    one stream: a partial read before it was published, or a stale one from
+    the previous call, breaks bit exactness."""
+    m, n, k = 16 * mb - 1, 16 * nb * tiles - 3, 128 * ksteps
+    p1 = exact_problem(m, n, k, seed=8100 + 100 * mb + 10 * nb + splits + tiles)
+    p2 = exact_problem(m, n, k, seed=8200 + 100 * mb + 10 * nb + splits + tiles)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1, waves=4)
+    assert plan.grid == tiles * splits and plan.flags == 0
     g1, g2 = run_gpu_pair(w8, p1, p2, plan, torch.cuda.Stream())
     check_full(p1, g1, exact=True)
     check_full(p2, g2, exact=True)
@@ -240,7 +253,7 @@ def test_exact_data_xcd_mixed_publication(w8, mb, nb, splits, ksteps):
                                    (8, 512, 8192), (16, 1536, 5120), (32, 768, 2048),
                                    (1, 128, 65536)])
 def test_default_split_plans_at_size_sampled(w8, m, n, k):
-    """Default plans that split K (narrow N, XCD-local publication): two
+    """Default plans that split K (narrow N, splits grouped per XCD): two
     problems back to back on one stream, sampled parity of both."""
     plan = w8.plan(m, n, k)
     assert plan.splits > 1 and plan.flags & w8.FLAG_XCD_LOCAL
@@ -352,16 +365,14 @@ def test_workload_full_parity(w8, idx):
     assert np.isfinite(oracle.bf16_bits_to_f64(g[:p.m, :p.n])).all()
 
 
-def test_largest_workload_sampled_parity(w8):
+def test_largest_workload_full_parity(w8):
+    """M=128, N=K=8192 (zero blocks, log-uniform scales): every one of the
+    1 048 576 outputs against the whole FP64 oracle (about 8.6 G
+    multiply-adds on the host cores)."""
     wl = datagen.workload(4)
     p = datagen.make_workload(wl)
     g = run_gpu(w8, p)
-    rows, cols = datagen.sample_indices(p.m, p.n, 6000, seed=5)
-    oc, tot, bound = oracle.gemm_at(p.a, p.w, p.scale, p.m, p.n, p.k, rows, cols,
-                                    a_row_stride=p.a_row_stride)
-    got = g[rows, cols]
-    ok = oracle.within_tolerance(got, oc, bound)
-    assert ok.all(), np.argwhere(~ok)[:5]
+    check_full(p, g)
     assert np.isfinite(oracle.bf16_bits_to_f64(g[:p.m, :p.n])).all()
 
 

@@ -545,3 +545,120 @@ def test_w8a8_pipeline_close_to_w8a16():
     _, t8, _ = oracle.gemm_w8a8(q, s, w, sw, m, n, k)
     _, t16, b16 = oracle.gemm(a, w, sw, m, n, k)
     assert (np.abs(t8 - t16) <= b16 * 2.0 ** -4 + 1e-30).all()
+
+
+# ------------------------------------------------------ the parity tolerance
+#
+# The bar every non-exact GPU test is graded with:
+#     |gpu - oracle| <= 2^-8 * B + ulp_bf16(oracle),   no NaN / Inf from the GPU,
+# with ulp(v) the BF16 spacing at v (2^(max(floor(log2|v|), -126) - 7)) and
+# ulp(0) = 2^-133.  The helpers are pinned against torch's BF16 decoding and
+# against hand-built values at the edge of the bar.
+
+def _torch_bf16_to_f64(bits):
+    t = torch.from_numpy(np.asarray(bits, dtype=np.uint16).view(np.int16).copy())
+    return t.view(torch.bfloat16).double().numpy()
+
+
+ALL_BF16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def test_bf16_bits_to_f64_equals_torch_and_scalar_decode_on_all_patterns():
+    got = oracle.bf16_bits_to_f64(ALL_BF16)
+    ref = _torch_bf16_to_f64(ALL_BF16)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    for b in range(0, 1 << 16, 257):
+        v = oracle.bf16_value(b)
+        assert (math.isnan(v) and math.isnan(got[b])) or v == got[b]
+
+
+def test_bf16_ulp_is_the_gap_to_the_next_bf16_value():
+    # every finite positive pattern except the largest: the gap to the next
+    # pattern (torch decode) is the ulp of the value, for both signs
+    pos = np.arange(0, 0x7F7F, dtype=np.uint32).astype(np.uint16)
+    v = _torch_bf16_to_f64(pos)
+    gap = _torch_bf16_to_f64(pos + 1) - v
+    assert np.array_equal(oracle.bf16_ulp(v), gap)
+    assert np.array_equal(oracle.bf16_ulp(-v), gap)
+    # the largest finite value: the gap below it (same binade)
+    top = _torch_bf16_to_f64(np.uint16([0x7F7F, 0x7F7E]))
+    assert oracle.bf16_ulp(top[0]) == top[0] - top[1] == 2.0 ** 120
+
+
+def test_bf16_ulp_anchors():
+    assert oracle.bf16_ulp(0.0) == 2.0 ** -133
+    assert oracle.bf16_ulp(-0.0) == 2.0 ** -133
+    assert oracle.bf16_ulp(2.0 ** -133) == 2.0 ** -133          # smallest subnormal
+    assert oracle.bf16_ulp(2.0 ** -127) == 2.0 ** -133          # subnormal
+    assert oracle.bf16_ulp(2.0 ** -126) == 2.0 ** -133          # smallest normal
+    assert oracle.bf16_ulp(1.0) == 2.0 ** -7
+    assert oracle.bf16_ulp(-1.0) == 2.0 ** -7
+    assert oracle.bf16_ulp(1.9921875) == 2.0 ** -7               # top of [1, 2)
+    assert oracle.bf16_ulp(2.0) == 2.0 ** -6
+    assert oracle.bf16_ulp(448.0) == 2.0 ** 1
+
+
+def _bits(x):
+    """BF16 bits of a float that is exactly a BF16 value."""
+    b = oracle.bf16_rne(x)
+    assert oracle.bf16_value(b) == x
+    return b
+
+
+def _passes(gpu, orc, bound):
+    return bool(oracle.within_tolerance(np.uint16([gpu]), np.uint16([orc]),
+                                        np.float64([bound]))[0])
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_within_tolerance_at_the_edge_of_the_bar(sign):
+    one = _bits(sign * 1.0)
+    # B = 6: 2^-8 B = 3 * 2^-7, plus ulp(1) = 2^-7 -> lim = 2^-5 exactly
+    assert _passes(_bits(sign * (1 + 2 ** -5)), one, 6.0)
+    assert not _passes(_bits(sign * (1 + 2 ** -5 + 2 ** -7)), one, 6.0)
+    assert _passes(_bits(sign * (1 - 2 ** -5)), one, 6.0)
+    assert not _passes(_bits(sign * (1 - 2 ** -5 - 2 ** -8)), one, 6.0)
+    # 2^-8, not 2^-7: B = 2 gives lim = 2^-7 + 2^-7; one more ulp fails
+    assert _passes(_bits(sign * (1 + 2 ** -6)), one, 2.0)
+    assert not _passes(_bits(sign * (1 + 2 ** -6 + 2 ** -7)), one, 2.0)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_within_tolerance_takes_the_ulp_of_the_oracle_value(sign):
+    two = _bits(sign * 2.0)
+    # ulp(2) = 2^-6; ulp of the GPU value 2 - 2^-6 would be 2^-7
+    assert _passes(_bits(sign * (2 - 2 ** -6)), two, 0.0)
+    assert not _passes(_bits(sign * (2 - 2 ** -6 - 2 ** -7)), two, 0.0)
+    # and an oracle value just below the binade: ulp 2^-7, not 2^-6
+    below = _bits(sign * (2 - 2 ** -7))
+    assert _passes(_bits(sign * 2.0), below, 0.0)
+    assert not _passes(_bits(sign * (2 + 2 ** -6)), below, 0.0)
+
+
+def test_within_tolerance_at_zero_and_subnormals():
+    assert _passes(0x0001, 0x0000, 0.0)                  # 2^-133 off zero
+    assert _passes(0x8001, 0x0000, 0.0)
+    assert not _passes(0x0002, 0x0000, 0.0)
+    assert _passes(0x8000, 0x0000, 0.0)                  # -0 vs +0
+    assert _passes(0x0003, 0x0002, 0.0)
+    assert not _passes(0x0004, 0x0002, 0.0)
+
+
+def test_within_tolerance_rejects_nan_and_inf():
+    one = _bits(1.0)
+    for bad in (0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80):
+        assert not _passes(bad, one, 1e30)
+    # an infinite oracle value is never produced by finite data; a GPU
+    # infinity against it still fails
+    assert not _passes(0x7F80, 0x7F80, 0.0)
+
+
+def test_within_tolerance_is_elementwise():
+    g = np.uint16([_bits(1.0), _bits(1.5), 0x7FC0, _bits(-3.0)])
+    o = np.uint16([_bits(1.0), _bits(1.0), _bits(1.0), _bits(-3.0 - 2 ** -6)])
+    b = np.float64([0.0, 1e3, 1e3, 0.0])
+    assert oracle.within_tolerance(g, o, b).tolist() == [True, True, False, True]
