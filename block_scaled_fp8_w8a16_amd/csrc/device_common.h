@@ -74,10 +74,11 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t grid)
 __device__ __forceinline__ void store_agent(f32x4_t *p, f32x4_t v)
 {
     uint64_t *q = reinterpret_cast<uint64_t *>(p);
-    const uint64_t lo = (uint64_t)__builtin_bit_cast(uint32_t, v.x) |
-                        ((uint64_t)__builtin_bit_cast(uint32_t, v.y) << 32);
-    const uint64_t hi = (uint64_t)__builtin_bit_cast(uint32_t, v.z) |
-                        ((uint64_t)__builtin_bit_cast(uint32_t, v.w) << 32);
+    // bit-cast the whole vector: clang reads element 0 for a bit_cast of a
+    // single vector element (v.y)
+    const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+    const uint64_t lo = (uint64_t)u.x | ((uint64_t)u.y << 32);
+    const uint64_t hi = (uint64_t)u.z | ((uint64_t)u.w << 32);
     __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
