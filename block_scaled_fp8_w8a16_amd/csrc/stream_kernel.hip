@@ -326,16 +326,18 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     }
 
     // ---- split-K: publish this split's tile, the last arrival adds all ----
-    // Each split stores its FP32 partial tile with agent-scope stores, which
-    // write through its XCD's L2, and waits until they have completed before
-    // its arrival is counted.  The last split to arrive acquires at agent
-    // scope (invalidating stale lines) and reads every split's partial with
-    // agent-scope loads, adding them in split order.  Nothing is written back
-    // from the L2 (a release fence would write back the whole L2, which
-    // measured microseconds per call over a grid), and the result does not
-    // depend on which XCD each split ran on.  The splits of a tile are
-    // consecutive logical workgroups, which the logical id map keeps on one
-    // XCD where the planner could arrange it.
+    // Each split stores its FP32 partial tile with agent-scope atomic stores
+    // (sc1: written through its XCD's L2) and waits until they have
+    // completed before its arrival is counted.  The last split to arrive
+    // reads every split's partial with agent-scope atomic loads (sc1: served
+    // from the coherent copy, never from a stale line of its own L1 or L2)
+    // issued after it has seen the count, and adds them in split order.
+    // There is no fence: the partials are themselves the atomics, and a
+    // release would write back (an acquire invalidate) the whole L2, each
+    // measured as serialized over the grid (microseconds per call).  The
+    // result does not depend on which XCD each split ran on.  The splits of
+    // a tile are consecutive logical workgroups, which the logical id map
+    // keeps on one XCD where the planner could arrange it.
     f32x4_t *ws_tile = reinterpret_cast<f32x4_t *>(g.ws) + (size_t)tile * g.splits * P * 64;
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES)
         store_agent(ws_tile + ((size_t)split * P + pi) * 64 + lane,
@@ -352,7 +354,6 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     __syncthreads();
     if (!last)
         return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
         f32x4_t s = load_agent(ws_tile + pi * 64 + lane);
         for (uint32_t sp = 1; sp < g.splits; ++sp)
