@@ -43,7 +43,7 @@ FLAG_XCD_LOCAL = 4
 
 # Symbols the C ABI exports (include/w8a16.h).
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
-           "w8a16_gemm_planned", "w8a16_plan_batched", "w8a16_gemm_batched",
+           "w8a16_gemm_planned", "w8a16_gemm_noalloc", "w8a16_plan_batched", "w8a16_gemm_batched",
            "w8a16_act_quant_fp8", "w8a16_plan_w8a8", "w8a16_gemm_w8a8",
            "w8a16_gemm_w8a8_planned", "w8a16_status_string", "w8a16_last_error")
 
@@ -105,6 +105,8 @@ def library() -> ctypes.CDLL:
         lib.w8a16_gemm_planned.argtypes = [vp, u32, vp, vp, vp, u32, u32, u32, u32,
                                            ctypes.POINTER(Plan), vp]
         lib.w8a16_gemm_planned.restype = ctypes.c_int
+        lib.w8a16_gemm_noalloc.argtypes = [vp, u32, vp, vp, vp, u32, u32, u32, u32, vp]
+        lib.w8a16_gemm_noalloc.restype = ctypes.c_int
         lib.w8a16_plan_batched.argtypes = [ctypes.POINTER(GemmDesc), u32, u32,
                                            ctypes.POINTER(Plan)]
         lib.w8a16_plan_batched.restype = ctypes.c_int
@@ -176,6 +178,18 @@ def gemm_raw(a_ptr: int, a_row_stride: int, w_ptr: int, scale_ptr: int, c_ptr: i
     return int(lib.w8a16_gemm_planned(a_ptr, a_row_stride, w_ptr, scale_ptr, c_ptr,
                                       c_row_stride, m, n, k, ctypes.byref(plan_),
                                       stream))
+
+
+def gemm_noalloc_raw(a_ptr: int, a_row_stride: int, w_ptr: int, scale_ptr: int, c_ptr: int,
+                     c_row_stride: int, m: int, n: int, k: int, stream: int = 0) -> int:
+    """w8a16_gemm_noalloc with device addresses (split-K scratch from the
+    library's static device array, no allocation); returns the status."""
+    return int(library().w8a16_gemm_noalloc(a_ptr, a_row_stride, w_ptr, scale_ptr, c_ptr,
+                                            c_row_stride, m, n, k, stream))
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20
+NOALLOC_COUNTERS = 1 << 18
 
 
 def gemm(a, w, scale, c=None, *, plan_: Optional[Plan] = None, stream=None):

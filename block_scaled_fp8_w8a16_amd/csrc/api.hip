@@ -123,6 +123,54 @@ int get_workspace(int dev, hipStream_t stream, const w8a16_plan_t &plan, Workspa
     return W8A16_OK;
 }
 
+// ---- scratch of w8a16_gemm_noalloc ---------------------------------------
+// One static device array per GPU (each device holds its own copy of the
+// code object's globals): FP32 split-K partials, then the arrival counters.
+// In host code `scratch` names a host-side stand-in, not device memory; its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchPartialBytes = (size_t)W8A16_NOALLOC_WORKSPACE_BYTES;
+constexpr size_t kScratchCounterWords = (size_t)W8A16_NOALLOC_COUNTERS;
+static __device__ __align__(256) uint8_t scratch[kScratchPartialBytes +
+                                                 kScratchCounterWords * sizeof(uint32_t)];
+
+__global__ __launch_bounds__(256) void w8a16_zero_words_kernel(uint32_t *p, uint32_t words)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < words)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mutex;
+std::map<int, uint8_t *> g_scratch;   // device address of `scratch`, per device
+
+// Device address of this device's scratch, looked up on the first call on
+// the device (the current device), which also clears the counters with a
+// fill kernel on `stream` (a kernel rather than a memset node, so that a
+// graph capturing this first call records a plain kernel).  The counters
+// start at zero and every kernel that uses them leaves them at zero.
+int device_scratch(int dev, hipStream_t stream, uint8_t **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return W8A16_OK;
+    }
+    uint8_t *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&ptr), HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    const uint32_t words = (uint32_t)kScratchCounterWords;
+    hipLaunchKernelGGL(w8a16_zero_words_kernel, dim3((words + 255u) / 256u), dim3(256), 0,
+                       stream, reinterpret_cast<uint32_t *>(ptr + kScratchPartialBytes), words);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "scratch counter clear");
+    g_scratch[dev] = ptr;
+    *out = ptr;
+    return W8A16_OK;
+}
+
 int check_call(const void *a, uint32_t a_row_stride, const void *w_fp8,
                const float *block_scale, void *c, uint32_t c_row_stride, uint32_t m,
                uint32_t n, uint32_t k)
@@ -136,9 +184,11 @@ int check_call(const void *a, uint32_t a_row_stride, const void *w_fp8,
     return W8A16_OK;
 }
 
+// Enqueue the plan's kernels.  `fixed`: the split-K workspace to use (the
+// no-alloc entry's scratch); null takes the (device, stream) workspace.
 int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *block_scale,
         void *c, uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
-        const w8a16_plan_t &plan, hipStream_t stream)
+        const w8a16_plan_t &plan, hipStream_t stream, const Workspace *fixed = nullptr)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -146,9 +196,13 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
         return hip_fail(e, "hipGetDevice");
     Workspace wsp;
     if (plan.splits > 1) {
-        int st = get_workspace(dev, stream, plan, &wsp);
-        if (st != W8A16_OK)
-            return st;
+        if (fixed) {
+            wsp = *fixed;
+        } else {
+            int st = get_workspace(dev, stream, plan, &wsp);
+            if (st != W8A16_OK)
+                return st;
+        }
     }
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
@@ -230,6 +284,51 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
                                         "activations (w8a16_gemm_w8a8_planned)");
     return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, p,
                static_cast<hipStream_t>(stream));
+}
+
+int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride, const void *w_fp8,
+                       const float *block_scale, void *c, uint32_t c_row_stride, uint32_t m,
+                       uint32_t n, uint32_t k, void *stream)
+{
+    using namespace w8a16;
+    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    if (st != W8A16_OK)
+        return fail_with_name(st, "w8a16_gemm_noalloc");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    uint32_t cus = 0;
+    st = device_cu_count(dev, &cus);
+    if (st != W8A16_OK)
+        return st;
+    w8a16_plan_t plan;
+    st = make_plan(m, n, k, cus, &plan);
+    if (st != W8A16_OK)
+        return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (plan.splits == 1)
+        return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan, hs);
+    if (plan.workspace_bytes > kScratchPartialBytes || plan.counter_count > kScratchCounterWords) {
+        char buf[256];
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm_noalloc: the plan for m=%u n=%u k=%u needs %llu bytes of split-K "
+                 "partials and %u counter words; the scratch holds %llu and %llu",
+                 m, n, k, (unsigned long long)plan.workspace_bytes, plan.counter_count,
+                 (unsigned long long)kScratchPartialBytes,
+                 (unsigned long long)kScratchCounterWords);
+        return fail(W8A16_ERR_WORKSPACE, buf);
+    }
+    uint8_t *ptr = nullptr;
+    st = device_scratch(dev, hs, &ptr);
+    if (st != W8A16_OK)
+        return st;
+    Workspace wsp;
+    wsp.ws = reinterpret_cast<float *>(ptr);
+    wsp.ws_bytes = kScratchPartialBytes;
+    wsp.counters = reinterpret_cast<uint32_t *>(ptr + kScratchPartialBytes);
+    wsp.counter_count = (uint32_t)kScratchCounterWords;
+    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan, hs, &wsp);
 }
 
 int w8a16_act_quant_fp8(const void *a, uint32_t a_row_stride, void *q, uint32_t q_row_stride,

@@ -179,6 +179,32 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride,
                        uint32_t m, uint32_t n, uint32_t k,
                        const w8a16_plan_t *plan, void *stream);
 
+/* ---- No-allocation entry point --------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * w8a16_gemm_noalloc() computes exactly what w8a16_gemm() computes, with
+ * the same default plan, arguments, checks (codes 1..6) and asynchronous
+ * launch, but the split-K partials and arrival counters of a plan that
+ * splits K come from a static device array the library holds on each GPU
+ * it runs on until the process ends (W8A16_NOALLOC_WORKSPACE_BYTES of
+ * partials plus W8A16_NOALLOC_COUNTERS 32-bit counter words, 17 MiB).  It
+ * calls no hipMalloc, hipFree or other allocating routine.  A plan needing
+ * more than that returns W8A16_ERR_WORKSPACE and enqueues nothing.  The
+ * first call on a device looks the array up and clears its counters with a
+ * small kernel on `stream`; every later call leaves them at zero.
+ *
+ * All calls on one GPU share its array: calls that overlap in time on that
+ * GPU (other streams, concurrent graph replays) race and give wrong
+ * results.  Order them (one stream, or events). */
+#define W8A16_NOALLOC_WORKSPACE_BYTES (16u << 20)
+#define W8A16_NOALLOC_COUNTERS (1u << 18)
+
+int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride,
+                       const void *w_fp8, const float *block_scale,
+                       void *c, uint32_t c_row_stride,
+                       uint32_t m, uint32_t n, uint32_t k, void *stream);
+
 /* ---- Batched tier ------------------------------------------------------
  * The pages' strided launch exists so that a multi-sequence Q/K/V tier can
  * hold it as one arm among several with their own pitches (page
