@@ -20,7 +20,11 @@ Prints one JSON line.  Usage:
     python bench.py --m-sweep N K          (default plan for m = 1..256, one line each)
     python bench.py --batched              (Q/K/V arms in one batched call vs three calls)
     python bench.py --w8a8                 (FP8 activation quantizer + W8A8 GEMM)
-    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR   (writes profiles/)
+    python bench.py --trace-run WORKLOAD [K]   (the timed region alone, for rocprofv3)
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR WORKLOAD   (writes profiles/)
+    python bench.py --summarize-trace TRACE_DIR WORKLOAD [K]          (writes profiles/)
+    python bench.py --summarize-mfma PMC_DIR WORKLOAD                 (writes profiles/)
+    python bench.py --summarize-pipeline ROOT                         (writes profiles/)
 """
 
 from __future__ import annotations
@@ -77,12 +81,36 @@ class Arena:
                       self.c[i].data_ptr()) for i in range(replicas)]
 
 
+SCRUB_BYTES = 512 << 20       # twice the 256 MiB Infinity Cache
+SPIN_UP_S = 0.02              # untimed GPU work right before a timed region
+
+
+class Scrub:
+    """A 512 MiB device buffer whose fill, enqueued right before a timed
+    region, evicts the Infinity Cache: the replicas the timed calls read
+    first then come from HBM, whatever the number of timed calls."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def run(self):
+        self.buf.fill_(0x5A5A5A5A)
+
+
 def time_workload(torch, w8, prob, steps: int, warmup: int, cold: bool = True,
-                  plan=None):
-    """Returns (arena, graph ms per call, eager ms per call, replicas)."""
+                  plan=None, scrub=None):
+    """Times `steps` calls: eagerly, then as one HIP graph of the same calls.
+    Call i reads replica i mod R of the operands, R replicas spanning
+    >= 512 MiB (twice the Infinity Cache).  Before each timed region the
+    GPU runs about 20 ms of untimed calls (so it is at its working clock,
+    not ramping up from idle) and then the 512 MiB scrub fill (so the first
+    replicas are not cache-resident).  Returns (arena, graph ms per call,
+    eager ms per call, replicas)."""
     per_replica = (prob.a.nbytes + prob.w.nbytes + prob.scale.nbytes + prob.c.nbytes)
     replicas = max(1, -(-ARENA_BYTES // per_replica)) if cold else 1
     arena = Arena(torch, prob, replicas)
+    if cold and scrub is None:
+        scrub = Scrub(torch)
     stream = torch.cuda.Stream()
     lib_args = (prob.a_row_stride, prob.c_row_stride, prob.m, prob.n, prob.k)
 
@@ -99,24 +127,52 @@ def time_workload(torch, w8, prob, steps: int, warmup: int, cold: bool = True,
         for i in range(warmup):          # also allocates any K-split workspace
             call(i)
         torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(steps):
-            call(warmup + i)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        eager_ms = start.elapsed_time(stop) / steps
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(steps):
-                call(warmup + i)
-        graph.replay()
+                call(i)
+
+        def spin_up():
+            t0 = time.perf_counter()
+            while True:
+                graph.replay()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= SPIN_UP_S:
+                    break
+            if scrub is not None:
+                scrub.run()
+
+        spin_up()
+        start.record(stream)
+        for i in range(steps):
+            call(i)
+        stop.record(stream)
         torch.cuda.synchronize()
+        eager_ms = start.elapsed_time(stop) / steps
+        spin_up()
         start.record(stream)
         graph.replay()
         stop.record(stream)
         torch.cuda.synchronize()
         graph_ms = start.elapsed_time(stop) / steps
     return arena, graph_ms, eager_ms, replicas
+
+
+def trace_run(wl_name: str, steps: int = 20, warmup: int = 5):
+    """The benchmark's timed region alone, for rocprofv3 --kernel-trace:
+    warm-up calls, the spin-up graph replays and the timed graph replay of
+    `steps` calls (each call on its own replica after the scrub), nothing
+    else.  The summary keeps each kernel's last `steps` dispatches: the
+    timed replay."""
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    w8.library()
+    wl = datagen.workload(wl_name)
+    prob = datagen.make_workload(wl)
+    arena, ms, _, _ = time_workload(torch, w8, prob, steps, warmup)
+    del arena
+    print("trace run done: %s %.3f us/call (graph replay)" % (wl_name, ms * 1e3), flush=True)
 
 
 def check_arena_output(arena, calls: int):
@@ -137,10 +193,11 @@ def check_arena_output(arena, calls: int):
     return ok
 
 
-def cpu_baseline(oracle, datagen, prob, budget_s: float = 10.0):
-    """The oracle as it stands, on the host cores, over whole GEMMs of the
-    headline workload, repeated until about `budget_s` seconds."""
-    threads = len(os.sched_getaffinity(0))
+def cpu_baseline(oracle, datagen, prob, budget_s: float = 10.0, threads: int = 0):
+    """The oracle as it stands, on the host cores (all of them unless
+    `threads` is given), over whole GEMMs of the headline workload, repeated
+    until about `budget_s` seconds."""
+    threads = threads or len(os.sched_getaffinity(0))
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -151,6 +208,28 @@ def cpu_baseline(oracle, datagen, prob, budget_s: float = 10.0):
             break
     dt = (time.perf_counter() - t0) / reps
     return dt, reps, threads
+
+
+def oracle_check(oracle, prob, c_bits, threads: int) -> dict:
+    """The GPU's C (BF16 bits, whole buffer) against the whole oracle:
+    fraction of outputs equal to the oracle's bits, the largest
+    |gpu - exact| / B (B = sum |a*w*s| of the output; the BF16 rounding of
+    the result is part of it), the largest error as a fraction of the
+    parity bar 2^-8 * B + ulp(oracle), and whether every output passes."""
+    import numpy as np
+    m, n = prob.m, prob.n
+    oc, tot, bound = oracle.gemm(prob.a, prob.w, prob.scale, m, n, prob.k,
+                                 a_row_stride=prob.a_row_stride, threads=threads)
+    g = c_bits[:m, :n]
+    gv = oracle.bf16_bits_to_f64(g)
+    ov = oracle.bf16_bits_to_f64(oc)
+    pos = bound > 0
+    err_b = float(np.max(np.abs(gv - tot)[pos] / bound[pos])) if pos.any() else 0.0
+    bar = np.ldexp(bound, -8) + oracle.bf16_ulp(ov)
+    return {"outputs": int(m * n), "bitexact_frac": round(float(np.mean(g == oc)), 6),
+            "max_err_over_B": err_b,
+            "max_err_over_bar": float(np.max(np.abs(gv - ov) / bar)),
+            "within_tolerance": bool(oracle.within_tolerance(g, oc, bound).all())}
 
 
 def load_traffic(workload: str, kernel_hash: str):
@@ -177,8 +256,9 @@ COPY_BYTES = 256 << 20
 
 
 def traffic_run(wl_name: str):
-    """A short run for rocprofv3 --pmc: 20 cold calls of the workload, then
-    three plain device copies of COPY_BYTES (the counters' calibration)."""
+    """A short run for rocprofv3 --pmc: the 512 MiB cache scrub, 20 cold calls
+    of the workload (each on its own replica), then three plain device
+    copies of COPY_BYTES (the counters' calibration)."""
     import torch
     import block_scaled_fp8_w8a16_amd as w8
     import datagen
@@ -187,6 +267,7 @@ def traffic_run(wl_name: str):
     per = prob.a.nbytes + prob.w.nbytes + prob.scale.nbytes + prob.c.nbytes
     replicas = max(1, -(-ARENA_BYTES // per))
     arena = Arena(torch, prob, replicas)
+    Scrub(torch).run()             # the first replicas are not cache-resident
     sp = torch.cuda.current_stream().cuda_stream
     for i in range(20):
         a, w, s, c = arena.ptrs[i % replicas]
@@ -227,7 +308,8 @@ PIPELINE_GROUPS = (
     "TCP_TCP_TA_DATA_STALL_CYCLES_sum",
     "TCC_HIT_sum TCC_MISS_sum TCC_TAG_STALL_sum GRBM_GUI_ACTIVE",
 )
-PIPELINE_WORKLOADS = ("m8_n4096_k4096", "m16_n12288_k5120", "m128_n8192_k8192")
+PIPELINE_WORKLOADS = ("m8_n4096_k4096", "m16_n12288_k5120", "m32_n6144_k2048_strided",
+                      "m128_n8192_k8192")
 
 
 def summarize_pipeline(root: str):
@@ -269,6 +351,61 @@ def summarize_pipeline(root: str):
     path = os.path.join(ROOT, "profiles", "memory_pipeline_counters.txt")
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE"
+CUS = 256              # MI355X
+SIMDS = 1024           # 4 per CU
+XCDS = 8
+
+
+def summarize_mfma(pmc_dir: str, wl_name: str):
+    """Writes profiles/mfma_<workload>.txt from one rocprofv3 --pmc run of
+    MFMA_COUNTERS over a --traffic-run of the workload: per GEMM kernel, the
+    MFMA-busy share of SIMD cycles (sum of SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE x SIMDs, the MfmaUtil expression of rocprofiler-sdk's
+    counter definitions) and the BF16 MFMA work it counted (MOPS x 512 =
+    flops) against 2*M*N*K."""
+    import csv
+    import glob
+    import datagen
+    wl = datagen.workload(wl_name)
+    vals = {}
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if "w8a16" not in r["Kernel_Name"]:
+                    continue
+                name = r["Kernel_Name"].replace("void ", "").replace(
+                    "w8a16::(anonymous namespace)::", "").split("(")[0]
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    path = os.path.join(ROOT, "profiles", "mfma_%s.txt" % wl.name)
+    with open(path, "w") as fh:
+        fh.write("# MFMA utilisation per GEMM dispatch on workload %s, rocprofv3 PMC\n" % wl.name)
+        fh.write("# command (run from /tmp with TMPDIR=/tmp):\n#   rocprofv3 --pmc %s "
+                 "--output-format csv -d PMC_DIR -- python3 bench.py --traffic-run %s ; "
+                 "python3 bench.py --summarize-mfma PMC_DIR %s\n" % (MFMA_COUNTERS, wl.name, wl.name))
+        fh.write("# values are means over the run's dispatches; rocprofv3 sums GRBM_GUI_ACTIVE over "
+                 "the %d XCDs and SQ_VALU_MFMA_BUSY_CYCLES over the %d SIMDs, so\n" % (XCDS, SIMDS))
+        fh.write("#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d * %d)   "
+                 "(rocprofiler-sdk's MfmaUtil, with the max over XCDs as the mean)\n" % (XCDS, SIMDS))
+        fh.write("#   mfma_util_cu_busy = (SQ_VALU_MFMA_BUSY_CYCLES / %d) / (SQ_BUSY_CU_CYCLES / %d)  "
+                 "(MFMA-busy share of the cycles the CUs were busy)\n" % (SIMDS, CUS))
+        fh.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        fh.write("flops_per_call: %d\n" % wl.flops())
+        for k in sorted(vals):
+            v = {c: sum(x) / len(x) for c, x in vals[k].items()}
+            busy, active = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0)
+            cu_busy = v.get("SQ_BUSY_CU_CYCLES", 0.0)
+            util = busy / (active / XCDS * SIMDS) if active else float("nan")
+            util_cu = (busy / SIMDS) / (cu_busy / CUS) if cu_busy else float("nan")
+            mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+            fh.write("kernel %s: dispatches %d, " % (k, len(next(iter(vals[k].values())))) +
+                     ", ".join("%s %.6g" % (c, x) for c, x in sorted(v.items())) +
+                     ", mfma_util %.4f, mfma_util_cu_busy %.4f, bf16_mfma_flops %.6g\n"
+                     % (util, util_cu, mops * 512))
     print(open(path).read())
 
 
@@ -327,9 +464,12 @@ def summarize_traffic(fetch_dir: str, write_dir: str, wl_name: str, command: str
     print(open(path).read())
 
 
-def summarize_trace(trace_dir: str, wl_name: str, command: str):
+def summarize_trace(trace_dir: str, wl_name: str, command: str, last: int = 0):
     """Writes profiles/kernel_trace_<workload>.txt from a rocprofv3
-    --kernel-trace --stats run: per-kernel dispatch counts and durations."""
+    --kernel-trace --stats run: per-kernel dispatch counts and durations.
+    last > 0 keeps only each kernel's `last` latest dispatches (the timed
+    graph replay of a --trace-run), and also gives the span from the first
+    to the last of them per dispatch (the time per call the replay saw)."""
     import csv
     import glob
     rows = []
@@ -338,21 +478,32 @@ def summarize_trace(trace_dir: str, wl_name: str, command: str):
             rows.extend(csv.DictReader(fh))
     by = {}
     for r in rows:
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-        by.setdefault(r["Kernel_Name"], []).append(d)
+        by.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     path = os.path.join(ROOT, "profiles", "kernel_trace_%s.txt" % wl_name)
+    spans = []
     with open(path, "w") as fh:
         fh.write("# rocprofv3 kernel trace of the benchmark on workload %s\n" % wl_name)
         fh.write("# command (run from /tmp with TMPDIR=/tmp):\n#   %s\n" % command)
         fh.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        if last:
+            fh.write("# each kernel's last %d dispatches: the timed graph replay\n" % last)
         fh.write("# kernel | dispatches | mean_us | median_us | min_us | max_us\n")
-        for k, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        for k, ts in sorted(by.items(), key=lambda kv: -len(kv[1])):
             if "w8a16" not in k:
                 continue
-            ds = sorted(ds)
+            ts = sorted(ts)
+            if last:
+                ts = ts[-last:]
+                spans.append((ts[0][0], ts[-1][1]))
+            ds = sorted((e - b) / 1000.0 for b, e in ts)
             short = k.replace("void ", "").replace("w8a16::(anonymous namespace)::", "")
             fh.write("%s | %d | %.3f | %.3f | %.3f | %.3f\n" % (
                 short, len(ds), sum(ds) / len(ds), ds[len(ds) // 2], ds[0], ds[-1]))
+        if spans and last:
+            b = min(x[0] for x in spans)
+            e = max(x[1] for x in spans)
+            fh.write("replay_span_us_per_call: %.3f\n" % ((e - b) / 1000.0 / last))
     print(open(path).read())
 
 
@@ -593,17 +744,27 @@ def main():
         k = int(sys.argv[3]) if len(sys.argv) > 3 else 8192
         m_sweep(n, k)
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-run":
+        trace_run(sys.argv[2] if len(sys.argv) > 2 else MAIN_WORKLOAD,
+                  int(sys.argv[3]) if len(sys.argv) > 3 else 20)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         wl_name = sys.argv[3] if len(sys.argv) > 3 else MAIN_WORKLOAD
-        if wl_name in ("batched", "w8a8"):       # the --batched / --w8a8 legs
+        if wl_name in ("batched", "w8a8", "w4a4"):      # the --batched / --w8a8 / --w4a4 legs
             cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- "
                    "python3 bench.py --%s ; python3 bench.py --summarize-trace TRACE_DIR %s"
                    % (wl_name, wl_name))
+            summarize_trace(sys.argv[2], wl_name, cmd)
         else:
+            steps = int(sys.argv[4]) if len(sys.argv) > 4 else 20
             cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d TRACE_DIR -- "
-                   "python3 bench.py --steps 50 --warmup 5 --no-cpu --only-main --workload %s ; "
-                   "python3 bench.py --summarize-trace TRACE_DIR %s" % (wl_name, wl_name))
-        summarize_trace(sys.argv[2], wl_name, cmd)
+                   "python3 bench.py --trace-run %s %d ; "
+                   "python3 bench.py --summarize-trace TRACE_DIR %s %d"
+                   % (wl_name, steps, wl_name, steps))
+            summarize_trace(sys.argv[2], wl_name, cmd, last=steps)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        summarize_mfma(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else "m128_n8192_k8192")
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pipeline":
         summarize_pipeline(sys.argv[2])
@@ -639,7 +800,7 @@ def main():
               % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
 
     import block_scaled_fp8_w8a16_amd as w8
@@ -651,19 +812,41 @@ def main():
     w8.library()
     khash = kernel_source_hash()
 
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    scrub = None if args.warm else Scrub(torch)
+
+    def measure(w, steps, warmup):
+        """Times one workload; keeps a host copy of the C written by call 0
+        (replica 0) for the CPU leg's check against the oracle."""
+        log("generating %s" % w.name)
+        pr = datagen.make_workload(w)
+        pl = w8.plan(w.m, w.n, w.k, cus)
+        log("timing %s plan=%s" % (w.name, pl.as_dict()))
+        ar, ms, eager, reps = time_workload(torch, w8, pr, steps, warmup, cold=not args.warm,
+                                            scrub=scrub)
+        ok = check_arena_output(ar, steps)
+        c0 = ar.c[0].cpu().numpy().view(np.uint16).reshape(pr.c.shape).copy()
+        per = pr.a.nbytes + pr.w.nbytes + pr.scale.nbytes + pr.c.nbytes
+        del ar
+        torch.cuda.empty_cache()
+        gb = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
+        tf = w.flops() / (ms * 1e-3) / 1e12
+        log("%s: %.3f us/call, %.1f GB/s, %.1f TFLOP/s (output sane %s)" %
+            (w.name, ms * 1e3, gb, tf, ok))
+        row = {"workload": w.name, "us_per_call": round(ms * 1e3, 3),
+               "us_per_call_eager": round(eager * 1e3, 3),
+               "gbs": round(gb, 1), "pct_hbm": round(100 * gb / HBM_PEAK_GBS, 2),
+               "tflops": round(tf, 3), "pct_mfma": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+               "output_sane": ok, "plan": pl.as_dict(), "arena_replicas": reps,
+               "timed_distinct_replica_bytes": min(steps, reps) * per, "seed": w.seed}
+        return pr, pl, ms, eager, reps, ok, c0, row
+
     wl = datagen.workload(args.workload)
-    log("generating %s" % wl.name)
-    prob = datagen.make_workload(wl)
-    plan = w8.plan(wl.m, wl.n, wl.k, torch.cuda.get_device_properties(0).multi_processor_count)
-    log("timing %s plan=%s" % (wl.name, plan.as_dict()))
-    arena, ms_call, eager_ms, replicas = time_workload(torch, w8, prob, args.steps,
-                                                       args.warmup, cold=not args.warm)
-    sane = check_arena_output(arena, args.steps + args.warmup)
-    del arena
-    torch.cuda.empty_cache()
+    prob, plan, ms_call, eager_ms, replicas, sane, c_main, main_row = measure(
+        wl, args.steps, args.warmup)
     alg_bytes = wl.algorithmic_bytes()
     gbs = alg_bytes / (ms_call * 1e-3) / 1e9
-    log("%s: %.3f us/call, %.1f GB/s (output sane %s)" % (wl.name, ms_call * 1e3, gbs, sane))
+    checked = [(wl, prob, c_main, main_row)]
 
     traffic = load_traffic(wl.name, khash)
     result = {
@@ -682,10 +865,14 @@ def main():
         "config": {"workload": wl.name, "m": wl.m, "n": wl.n, "k": wl.k,
                    "a_row_stride": wl.a_row_stride, "c_row_stride": wl.c_row_stride,
                    "seed": wl.seed, "weights": "warm" if args.warm else "cold",
-                   "arena_replicas": replicas},
+                   "arena_replicas": replicas,
+                   "timed_distinct_replica_bytes": main_row["timed_distinct_replica_bytes"],
+                   "cache_scrub_bytes": 0 if args.warm else SCRUB_BYTES},
         "us_per_call": round(ms_call * 1e3, 3),
         "us_per_call_eager": round(eager_ms * 1e3, 3),
-        "timing": "HIP graph of the K calls, replayed; HIP events on the launch stream",
+        "timing": ("HIP graph of the K calls, replayed once; HIP events on the launch stream; "
+                   "before it ~20 ms of untimed replays (working clock) and a 512 MiB fill "
+                   "that evicts the Infinity Cache; call i reads replica i mod R"),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(wl.flops() / (ms_call * 1e-3) / 1e12, 3),
         "plan": plan.as_dict(),
@@ -709,49 +896,39 @@ def main():
         rows = []
         for other in datagen.WORKLOADS:
             if other.name == wl.name:
-                rows.append({"workload": wl.name, "us_per_call": round(ms_call * 1e3, 3),
-                         "us_per_call_eager": round(eager_ms * 1e3, 3),
-                             "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2),
-                             "tflops": result["tflops"],
-                             "pct_mfma": round(100 * result["tflops"] / BF16_PEAK_TFLOPS, 2),
-                             "output_sane": sane, "plan": plan.as_dict(), "seed": wl.seed})
+                rows.append(main_row)
                 continue
-            log("generating %s" % other.name)
-            op = datagen.make_workload(other)
-            oplan = w8.plan(other.m, other.n, other.k)
             steps = max(20, min(args.steps, 200))
             owarm = max(5, args.warmup // 2)
-            ar, oms, oeager, orep = time_workload(torch, w8, op, steps, owarm)
-            ok = check_arena_output(ar, steps + owarm)
-            del ar
-            torch.cuda.empty_cache()
-            ogbs = other.algorithmic_bytes() / (oms * 1e-3) / 1e9
-            otf = other.flops() / (oms * 1e-3) / 1e12
-            log("%s: %.3f us/call, %.1f GB/s, %.1f TFLOP/s (output sane %s)" %
-                (other.name, oms * 1e3, ogbs, otf, ok))
-            rows.append({"workload": other.name, "us_per_call": round(oms * 1e3, 3),
-                         "us_per_call_eager": round(oeager * 1e3, 3),
-                         "gbs": round(ogbs, 1), "pct_hbm": round(100 * ogbs / HBM_PEAK_GBS, 2),
-                         "tflops": round(otf, 3),
-                         "pct_mfma": round(100 * otf / BF16_PEAK_TFLOPS, 2),
-                         "output_sane": ok, "plan": oplan.as_dict(),
-                         "arena_replicas": orep, "seed": other.seed})
-            del op
+            op, _, _, _, _, _, oc0, orow = measure(other, steps, owarm)
+            rows.append(orow)
+            checked.append((other, op, oc0, orow))
         result["all_workloads"] = rows
 
     if not args.no_cpu:
         import oracle   # the CPU baseline leg is the only part that runs the oracle
         log("timing the CPU oracle on %s" % wl.name)
         dt, reps, threads = cpu_baseline(oracle, datagen, prob)
+        log("timing the CPU oracle on %s, one thread" % wl.name)
+        dt1, reps1, _ = cpu_baseline(oracle, datagen, prob, budget_s=5.0, threads=1)
         result["cpu_baseline"] = {
             "value": round(alg_bytes / dt / 1e9, 4),
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": "%d whole %s GEMMs (FP64 C oracle, OpenMP), %.3f s each" %
-                      (reps, wl.name, dt),
+            "sample": "%d whole %s GEMMs (FP64 C oracle, OpenMP, %d threads), %.3f s each" %
+                      (reps, wl.name, threads, dt),
             "us_per_call": round(dt * 1e6, 1),
+            "single_thread": {"value": round(alg_bytes / dt1 / 1e9, 4), "unit": "GB/s",
+                              "us_per_call": round(dt1 * 1e6, 1),
+                              "sample": "%d whole GEMMs, 1 thread" % reps1},
         }
+        # The same leg grades what each timed workload's call 0 wrote
+        # against the whole oracle (a diagnostic; parity itself is the GPU
+        # tests' job).
+        for w, pr, c0, row in checked:
+            log("oracle check of %s" % w.name)
+            row["oracle_check"] = oracle_check(oracle, pr, c0, threads)
     print(json.dumps(result), flush=True)
 
 

@@ -355,9 +355,20 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &g, uint32_t lid)
     if (!last)
         return;
     for (uint32_t pi = wave; pi < (uint32_t)P; pi += WAVES) {
+        // eight partial loads in flight at a time (each is a round trip to
+        // the coherent copy), added in split order
         f32x4_t s = load_agent(ws_tile + pi * 64 + lane);
-        for (uint32_t sp = 1; sp < g.splits; ++sp)
-            s += load_agent(ws_tile + ((size_t)sp * P + pi) * 64 + lane);
+        for (uint32_t sp = 1; sp < g.splits; sp += 8) {
+            f32x4_t v[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                if (sp + u < g.splits)
+                    v[u] = load_agent(ws_tile + ((size_t)(sp + u) * P + pi) * 64 + lane);
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                if (sp + u < g.splits)
+                    s += v[u];
+        }
         const uint32_t j = pi / MB, b = pi % MB;
         store_c4(g, s, m0 + 16u * b + out_row_off, n0 + 16u * j + out_col_off);
     }
