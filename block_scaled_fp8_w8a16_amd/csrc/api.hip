@@ -225,6 +225,8 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
         e = launch_stream(g, plan, stream);
     else if (plan.kernel == W8A16_KERNEL_RING)
         e = launch_ring(g, plan, stream);
+    else if (plan.n_blocks == kWideNBlocks)
+        e = launch_wide(g, plan, stream);
     else
         e = plan.m_blocks == 4 ? launch_tile_m64(g, plan, stream)
                                : launch_tile_m128(g, plan, stream);

@@ -74,5 +74,11 @@ hipError_t launch_stream_batched(const BatchArgs &b, const w8a16_plan_t &p, hipS
 hipError_t launch_tile_m64(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m128(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_ring(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+// 128 x 256 tiles (tile plans with m_blocks 8, n_blocks 16).
+hipError_t launch_wide(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
+// Adds the K splits of a tile plan's workspace ([splits][ws_rows][ws_cols]
+// FP32, whole tiles) in split order and stores C.
+hipError_t launch_split_reduce(const GemmArgs &g, uint32_t ws_cols, uint32_t ws_rows,
+                               hipStream_t stream);
 
 }  // namespace w8a16

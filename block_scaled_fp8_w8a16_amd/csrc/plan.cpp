@@ -136,7 +136,8 @@ static uint32_t w8a8_lds_bytes(uint32_t mb, uint32_t nb, uint32_t waves)
 
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
 {
-    return (mb == 4 || mb == 8) && (nb == 4 || nb == 8);
+    return ((mb == 4 || mb == 8) && (nb == 4 || nb == 8)) ||
+           (mb == kWideMBlocks && nb == kWideNBlocks);
 }
 
 int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
@@ -216,35 +217,57 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      "variant", p->m_blocks, p->n_blocks);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
-        if (p->flags != 0 ||
-            (p->waves != 0 && p->waves != 4 && p->waves != 6 && p->waves != 8 &&
-             p->waves != 10)) {
-            snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel takes no flags and 4, 6, 8 or 10 waves "
-                     "(flags=0x%x, waves=%u)", p->flags, p->waves);
-            return fail(W8A16_ERR_BAD_PLAN, buf);
+        if (p->m_blocks == kWideMBlocks && p->n_blocks == kWideNBlocks) {
+            // the wide tile: fixed rings (3 weight steps, 3 A halves), 4 waves
+            if (p->depth == 0)
+                p->depth = 3;
+            if (p->a_depth == 0)
+                p->a_depth = 3;
+            if (p->waves == 0)
+                p->waves = 4;
+            if (p->flags != 0 || p->depth != 3 || p->a_depth != 3 || p->waves != 4) {
+                snprintf(buf, sizeof buf,
+                         "w8a16_plan: the 128 x 256 tile takes depth 3, a_depth 3, 4 waves and "
+                         "no flags (depth=%u, a_depth=%u, waves=%u, flags=0x%x)", p->depth,
+                         p->a_depth, p->waves, p->flags);
+                return fail(W8A16_ERR_BAD_PLAN, buf);
+            }
+            p->stage_steps = 0;
+            p->block = 256;
+            p->lds_bytes = wide_lds_bytes();
+        } else {
+            if (p->flags != 0 ||
+                (p->waves != 0 && p->waves != 4 && p->waves != 6 && p->waves != 8 &&
+                 p->waves != 10)) {
+                snprintf(buf, sizeof buf,
+                         "w8a16_plan: tile kernel takes no flags and 4, 6, 8 or 10 waves "
+                         "(flags=0x%x, waves=%u)", p->flags, p->waves);
+                return fail(W8A16_ERR_BAD_PLAN, buf);
+            }
+            // Built (weight buffers, A buffers) pairs; all fit in LDS.
+            if (p->a_depth == 0)
+                p->a_depth = 2;
+            const uint32_t ast = p->a_depth;
+            if (!tile_depth_built(p->m_blocks, p->n_blocks, p->depth, ast)) {
+                snprintf(buf, sizeof buf,
+                         "w8a16_plan: tile kernel has no depth=%u variant for m_blocks=%u, "
+                         "n_blocks=%u with %u A buffers", p->depth, p->m_blocks, p->n_blocks,
+                         ast);
+                return fail(W8A16_ERR_BAD_PLAN, buf);
+            }
+            if (p->waves == 0)
+                p->waves = 4;
+            if (!tile_variant_ok(p->m_blocks, p->n_blocks, p->depth, ast, p->waves)) {
+                snprintf(buf, sizeof buf,
+                         "w8a16_plan: tile kernel has no %u-wave variant for m_blocks=%u, "
+                         "n_blocks=%u with %u A buffers", p->waves, p->m_blocks, p->n_blocks,
+                         ast);
+                return fail(W8A16_ERR_BAD_PLAN, buf);
+            }
+            p->stage_steps = 0;
+            p->block = p->waves * 64;
+            p->lds_bytes = tile_lds_bytes(p->m_blocks, p->n_blocks, p->depth, ast);
         }
-        // Built (weight buffers, A buffers) pairs; all fit in LDS.
-        if (p->a_depth == 0)
-            p->a_depth = 2;
-        const uint32_t ast = p->a_depth;
-        if (!tile_depth_built(p->m_blocks, p->n_blocks, p->depth, ast)) {
-            snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel has no depth=%u variant for m_blocks=%u, "
-                     "n_blocks=%u with %u A buffers", p->depth, p->m_blocks, p->n_blocks, ast);
-            return fail(W8A16_ERR_BAD_PLAN, buf);
-        }
-        if (p->waves == 0)
-            p->waves = 4;
-        if (!tile_variant_ok(p->m_blocks, p->n_blocks, p->depth, ast, p->waves)) {
-            snprintf(buf, sizeof buf,
-                     "w8a16_plan: tile kernel has no %u-wave variant for m_blocks=%u, "
-                     "n_blocks=%u with %u A buffers", p->waves, p->m_blocks, p->n_blocks, ast);
-            return fail(W8A16_ERR_BAD_PLAN, buf);
-        }
-        p->stage_steps = 0;
-        p->block = p->waves * 64;
-        p->lds_bytes = tile_lds_bytes(p->m_blocks, p->n_blocks, p->depth, ast);
         if (p->lds_bytes > kMaxLdsBytes) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: %u bytes of LDS per workgroup exceed the %u available",

@@ -31,6 +31,13 @@ constexpr uint32_t tile_lds_bytes(uint32_t m_blocks, uint32_t n_blocks, uint32_t
     return a_stages * 16 * m_blocks * 256 + w_stages * 16 * n_blocks * 128 + 256;
 }
 
+// LDS of the wide tile kernel (128 x 256 C tile, m_blocks 8, n_blocks 16):
+// three K steps of weight (256 rows x 128 bytes), three K halves of A (128
+// rows x 128 bytes) and the two 128-column blocks' scale rows (64 floats
+// each).
+constexpr uint32_t wide_lds_bytes() { return 3 * 256 * 128 + 3 * 128 * 128 + 2 * 256; }
+constexpr uint32_t kWideMBlocks = 8, kWideNBlocks = 16;
+
 // Built tile-kernel ring sizes (weight buffers = depth, A buffers =
 // a_depth) per tile shape; tiles are 64 or 128 rows by 64 or 128 columns.
 // The list is the dispatch table of the tile kernel's launcher.

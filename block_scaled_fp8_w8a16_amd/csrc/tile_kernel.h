@@ -387,25 +387,6 @@ __global__ __launch_bounds__(64 * (4 * KH + (PROD ? 2 : 0))) void w8a16_tile_ker
                                          col_off + 16u * j) = acc[j][b];
 }
 
-// C = sum over splits, in split order, of the workspace tiles; one thread
-// per 4 adjacent outputs.
-__global__ __launch_bounds__(256) void w8a16_split_reduce_kernel(GemmArgs g, uint32_t ws_cols,
-                                                                 uint32_t ws_rows)
-{
-    const uint32_t quads = ws_cols / 4u;
-    const uint64_t id = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t row = (uint32_t)(id / quads);
-    const uint32_t col = (uint32_t)(id % quads) * 4u;
-    if (row >= g.m || col >= g.n)
-        return;
-    const size_t plane = (size_t)ws_rows * ws_cols;
-    const float *p = g.ws + (size_t)row * ws_cols + col;
-    f32x4_t s = *reinterpret_cast<const f32x4_t *>(p);
-    for (uint32_t sp = 1; sp < g.splits; ++sp)
-        s += *reinterpret_cast<const f32x4_t *>(p + sp * plane);
-    store_c4(g, s, row, col);
-}
-
 template <int MT, int NT, int WST, int AST, int KH, bool PROD, bool NTW>
 hipError_t launch_tile_n(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
@@ -424,13 +405,7 @@ hipError_t launch_tile_n(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t s
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1)
         return e;
-    const uint32_t ws_cols = p.n_tiles * NT;
-    const uint32_t ws_rows = p.m_tiles * MT;
-    const uint64_t threads = (uint64_t)g.m * (ws_cols / 4u);
-    const uint32_t blocks = (uint32_t)((threads + 255u) / 256u);
-    hipLaunchKernelGGL(w8a16_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, g, ws_cols,
-                       ws_rows);
-    return hipGetLastError();
+    return launch_split_reduce(g, p.n_tiles * NT, p.m_tiles * MT, stream);
     }
 }
 

@@ -349,6 +349,26 @@ def test_xcd_local_plans_need_whole_tiles_per_xcd():
                      flags=w8.FLAG_XCD_LOCAL, waves=8)
 
 
+def test_wide_tile_plans():
+    # 128 x 256 tiles: 32 column tiles x 8 splits of 8 steps at 128 x 8192 x 8192
+    p = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 16, 8, depth=3, a_depth=3)
+    assert (p.grid, p.block, p.lds_bytes, p.waves) == (256, 256, 147968, 4)
+    assert (p.m_tiles, p.n_tiles, p.steps_per_split) == (1, 32, 8)
+    assert p.workspace_bytes == 8 * 128 * 8192 * 4
+    # ragged: 200 rows, 1031 columns -> 2 x 5 tiles
+    p = w8.make_plan(200, 1031, 1024, w8.KERNEL_TILE, 8, 16, 3, depth=0, a_depth=0, waves=0)
+    assert (p.m_tiles, p.n_tiles, p.splits, p.depth, p.a_depth, p.waves) == (2, 5, 3, 3, 3, 4)
+    assert p.workspace_bytes == 3 * 256 * 1280 * 4
+    for depth, a_depth, waves, flags in [(4, 3, 4, 0), (3, 2, 4, 0), (3, 3, 8, 0), (3, 3, 4, 1)]:
+        with pytest.raises(w8.W8A16Error) as e:
+            w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 16, 8, depth=depth,
+                         a_depth=a_depth, waves=waves, flags=flags)
+        assert e.value.status == w8.ERR_BAD_PLAN
+    # at most 64 K steps per split
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(128, 8192, 8192 * 2, w8.KERNEL_TILE, 8, 16, 1, depth=3, a_depth=3)
+
+
 def test_explicit_plans():
     p = w8.make_plan(16, 4096, 4096, w8.KERNEL_STREAM, 1, 4, 8)
     _covers(p, 16, 4096, 4096)

@@ -6,6 +6,8 @@ NaN or infinite.  Data whose FP32 accumulation is exact must match the
 oracle bit for bit, which the graded tolerance alone would not force.
 """
 
+import warnings
+
 import numpy as np
 import pytest
 
@@ -210,7 +212,7 @@ def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
 
 def test_xcd_local_splits_on_concurrent_streams(w8):
     """Split plans on two streams at once (each stream has its own split
-    workspace and counters): four calls per stream, interleaved, with no
+    split workspace and counters): four calls per stream, interleaved, with no
     synchronisation between them; every result bit-exact."""
     m, n, k = 13, 16 * 4 * 8 - 3, 128 * 32
     plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, 1, 4, 4, depth=1,
@@ -336,6 +338,39 @@ def test_exact_data_every_tile_variant(w8, mb, nb, depth, a_depth, splits, m, wa
     assert plan.block == 64 * waves
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
+
+
+@pytest.mark.parametrize("m", [1, 65, 128, 200])
+@pytest.mark.parametrize("splits", [1, 2, 3])
+@pytest.mark.parametrize("n,ksteps", [(507, 8), (300, 7), (256, 1), (1031, 5)])
+def test_exact_data_wide_tile(w8, m, splits, n, ksteps):
+    """128 x 256 tiles (32x32x16 MFMAs, weight ring of 3 steps, A ring of 3
+    half steps): ragged rows and columns, one and several row tiles, K
+    splits including uneven ones, one-step splits, bit-exact."""
+    k = 128 * ksteps
+    p = exact_problem(m, n, k, seed=31 * m + n + 7 * splits + ksteps, a_row_stride=k + 40,
+                      c_row_stride=n + 9, c_extra_rows=2)
+    try:
+        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, 16, splits, depth=3, a_depth=3)
+    except w8.W8A16Error as e:
+        assert e.status == w8.ERR_BAD_PLAN and splits > ksteps
+        pytest.skip("more splits than K steps")
+    assert plan.block == 256 and plan.lds_bytes == 147968
+    g = run_gpu(w8, p, plan)
+    check_full(p, g, exact=True)
+    assert np.array_equal(g, run_gpu(w8, p, plan))
+
+
+def test_wide_tile_long_k_and_strides(w8):
+    """Rings that wrap many times (40 and 64 steps per split), pitches."""
+    for m, n, ksteps, splits in [(130, 300, 40, 1), (128, 512, 128, 2), (97, 769, 40, 3)]:
+        k = 128 * ksteps
+        p = datagen.make_problem(m, n, k, seed=m + n + k, a_row_stride=k + 24,
+                                 c_row_stride=n + 11, c_extra_rows=2)
+        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, 16, splits, depth=3, a_depth=3)
+        g = run_gpu(w8, p, plan)
+        check_full(p, g)
+        assert np.array_equal(g, run_gpu(w8, p, plan))
 
 
 def test_tile_kernel_long_k_and_strides(w8):
@@ -468,10 +503,10 @@ def test_non_default_stream_and_torch_wrapper(w8):
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 8192), (32, 768, 2048), (8, 4096, 4096),
                                    (96, 4096, 6144)])
 def test_graph_replays_match_eager(w8, m, n, k):
-    """Calls captured into a HIP graph after a warm-up call (split workspace,
-    arrival counters and dispatch probe set up outside the capture), then
+    """Calls captured into a HIP graph after a warm-up call (split workspace
+    set up outside the capture), then
     replayed three times with eager calls and synchronisations between the
-    replays: every replay gives the eager call's bits.  Covers XCD-local K
+    replays: every replay gives the eager call's bits.  Covers stream K
     splits (narrow N), an unsplit stream plan and the tile kernel with its
     split-reduction kernel."""
     probs = [datagen.make_problem(m, n, k, seed=900 + i + m) for i in range(3)]
@@ -511,6 +546,83 @@ def test_graph_replays_match_eager(w8, m, n, k):
         oc, _, bound = oracle.gemm_at(p.a, p.w, p.scale, m, n, k, rows, cols,
                                       a_row_stride=p.a_row_stride)
         assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+
+
+def _bufs(p):
+    return dev_u16(p.a), dev(p.w), dev(p.scale), dev_u16(p.c)
+
+
+def _call_on(w8, p, bufs, stream):
+    a, w, s, c = bufs
+    return w8.gemm_raw(a.data_ptr(), p.a_row_stride, w.data_ptr(), s.data_ptr(), c.data_ptr(),
+                       p.c_row_stride, p.m, p.n, p.k, stream.cuda_stream)
+
+
+def test_graph_survives_workspace_growth(w8):
+    """A graph captured with a small split plan keeps working after a larger
+    plan has grown that stream's workspace (the old buffer stays alive), and
+    a call that would have to grow the workspace during capture is refused
+    with W8A16_ERR_WORKSPACE and enqueues nothing."""
+    small = datagen.make_problem(8, 512, 4096, seed=61)        # stream kernel, 4 K splits
+    big = datagen.make_problem(16, 1024, 8192, seed=62)        # 4 K splits, twice the slots
+    assert w8.plan(8, 512, 4096).splits > 1
+    assert w8.plan(16, 1024, 8192).workspace_bytes > w8.plan(8, 512, 4096).workspace_bytes
+    sb, bb = _bufs(small), _bufs(big)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        assert _call_on(w8, small, sb, stream) == 0, w8.last_error()
+        torch.cuda.synchronize()
+        want = sb[3].cpu().numpy()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            assert _call_on(w8, small, sb, stream) == 0, w8.last_error()
+        assert _call_on(w8, big, bb, stream) == 0, w8.last_error()     # grows the workspace
+        torch.cuda.synchronize()
+        big_first = bb[3].cpu().numpy()
+        for rep in range(3):
+            sb[3].fill_(0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(sb[3].cpu().numpy(), want), "replay %d" % rep
+            assert _call_on(w8, big, bb, stream) == 0, w8.last_error()
+            torch.cuda.synchronize()
+            assert np.array_equal(bb[3].cpu().numpy(), big_first)
+    check_full(small, want.view(np.uint16).reshape(small.c.shape))
+    # a fresh stream has no workspace: capturing a split call there is refused
+    fresh = torch.cuda.Stream()
+    c_before = bb[3].clone()
+    g2 = torch.cuda.CUDAGraph()
+    with warnings.catch_warnings():
+        warnings.filterwarnings("ignore", message="The CUDA Graph is empty")
+        with torch.cuda.graph(g2, stream=fresh):
+            st = _call_on(w8, big, bb, fresh)
+    assert st == w8.ERR_WORKSPACE, (st, w8.last_error())
+    assert "capturing" in w8.last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(bb[3], c_before)
+
+
+def test_tile_splits_then_stream_splits_on_one_stream(w8):
+    """Tile and stream split plans alternating on one stream share its split
+    workspace (partials, then the stream kernel's counters): every result
+    exact."""
+    t = exact_problem(128, 4096, 1024, seed=63)
+    sp = exact_problem(8, 512, 1024, seed=64)
+    tplan = w8.make_plan(128, 4096, 1024, w8.KERNEL_TILE, 4, 8, 2, depth=4, a_depth=4, waves=10)
+    splan = w8.make_plan(8, 512, 1024, w8.KERNEL_STREAM, 1, 1, 4, depth=1, waves=8)
+    stream = torch.cuda.Stream()
+    tb, sbuf = _bufs(t), _bufs(sp)
+    for _ in range(2):
+        for prob, bufs, plan in ((t, tb, tplan), (sp, sbuf, splan)):
+            a, w, s, c = bufs
+            st = w8.gemm_raw(a.data_ptr(), prob.a_row_stride, w.data_ptr(), s.data_ptr(),
+                             c.data_ptr(), prob.c_row_stride, prob.m, prob.n, prob.k,
+                             stream.cuda_stream, plan)
+            assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    check_full(t, tb[3].cpu().numpy().view(np.uint16).reshape(t.c.shape), exact=True)
+    check_full(sp, sbuf[3].cpu().numpy().view(np.uint16).reshape(sp.c.shape), exact=True)
 
 
 def test_argument_errors_with_device_pointers(w8):

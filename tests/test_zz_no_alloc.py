@@ -37,9 +37,11 @@ def _call(w8, fn, p, bufs, stream):
 
 
 # (larger, smaller) pairs: stream-kernel K splits (narrow N), tile-kernel
-# splits added by the reduction kernel, and a plan without splits.
+# splits added by the reduction kernel, tile splits followed by stream splits,
+# and a plan without splits.
 PAIRS = [((16, 1024, 8192), (4, 512, 4096)),
          ((128, 4096, 8192), (72, 3072, 6144)),
+         ((128, 4096, 8192), (16, 1024, 8192)),
          ((8, 4096, 4096), (3, 1000, 1024))]
 
 
