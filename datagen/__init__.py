@@ -197,3 +197,98 @@ def sample_indices(m: int, n: int, count: int, seed: int
     cols.append(rng.integers(0, n, count))
     return (np.concatenate(rows).astype(np.uint32),
             np.concatenate(cols).astype(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# W4A4 MX operands (page "w4a4_proj/mx_plan.rs" plans the projection; the
+# format read as OCP MXFP4): FP4 E2M1 elements, two per byte with the even
+# element in the low nibble, one E8M0 scale byte per 32 consecutive K
+# elements of a row.
+#
+# Recipe: A float32 N(0, 1) [m, k] (drawn first), W float32 N(0, 0.02)
+# [n, k] (drawn second), each quantized per 32-element block as the MX
+# format's conversion does: shared exponent e = floor(log2(amax)) - 2 (2 is
+# E2M1's largest exponent), clamped to [-127, 127], scale byte e + 127;
+# elements = E2M1 round-to-nearest-even of v / 2^e, saturated to +-6; an
+# all-zero block gets scale byte 0 (2^-127) and zero elements.  A's row
+# pitch is in elements (even); pad bytes hold 0x77 (6.0 in both nibbles),
+# which would change the result if read.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+A_PAD_FP4 = 0x77
+
+# E2M1 magnitude code boundaries for round-to-nearest-even: |x| in
+# (lo, hi) goes to the code; a tie goes to the even code.
+_E2M1_MAGS = np.float32([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def to_e2m1_codes(x: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (uint8, 0..15) nearest to float32 ``x``, ties to the
+    even code, saturating to +-6."""
+    x = np.asarray(x, dtype=np.float32)
+    mag = np.abs(x)
+    d = np.abs(mag[..., None] - _E2M1_MAGS)            # distances to the 8 magnitudes
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among equidistant codes take the even one (ties occur between a pair)
+    even = cand & ((np.arange(8) % 2) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    code = np.where(mag > 6.0, 7, code).astype(np.uint8)
+    return (code | np.where(np.signbit(x), np.uint8(8), np.uint8(0))).astype(np.uint8)
+
+
+def quantize_mx(xf: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP4 quantization of float32 [r, k] (k % 32 == 0): returns (packed
+    codes uint8 [r, k/2], scale bytes uint8 [r, k/32])."""
+    r, k = xf.shape
+    assert k % MX_BLOCK == 0
+    blocks = xf.reshape(r, k // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2.0
+    e = np.clip(np.where(amax > 0, e, -127.0), -127.0, 127.0)
+    scaled = (blocks / np.exp2(e)[..., None].astype(np.float32)).astype(np.float32)
+    codes = to_e2m1_codes(scaled).reshape(r, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(packed), np.ascontiguousarray((e + 127).astype(np.uint8))
+
+
+@dataclasses.dataclass
+class MxProblem:
+    """Host operands of one W4A4 call: ``a`` [m, a_row_stride / 2] packed
+    FP4 bytes, ``a_scale`` [m, k/32], ``w`` [n, k/2], ``w_scale`` [n, k/32]
+    (E8M0 bytes), ``c`` [m + c_extra_rows, c_row_stride] BF16 bits."""
+    m: int
+    n: int
+    k: int
+    a_row_stride: int
+    c_row_stride: int
+    a: np.ndarray
+    a_scale: np.ndarray
+    w: np.ndarray
+    w_scale: np.ndarray
+    c: np.ndarray
+    seed: int
+
+    def algorithmic_bytes(self) -> int:
+        """FP4 weight and activations once, their scales once, C once."""
+        return (self.n * self.k // 2 + self.n * self.k // MX_BLOCK + self.m * self.k // 2 +
+                self.m * self.k // MX_BLOCK + 2 * self.m * self.n)
+
+
+def make_mx_problem(m: int, n: int, k: int, seed: int, a_row_stride: Optional[int] = None,
+                    c_row_stride: Optional[int] = None, w_std: float = 0.02,
+                    c_extra_rows: int = 0) -> MxProblem:
+    a_row_stride = k if a_row_stride is None else a_row_stride
+    c_row_stride = n if c_row_stride is None else c_row_stride
+    assert a_row_stride % 2 == 0 and a_row_stride >= k
+    rng = np.random.default_rng(seed)
+    af = rng.standard_normal((m, k), dtype=np.float32)
+    apk, asc = quantize_mx(af)
+    a = np.full((m, a_row_stride // 2), A_PAD_FP4, dtype=np.uint8)
+    a[:, :k // 2] = apk
+    wf = rng.standard_normal((n, k), dtype=np.float32) * np.float32(w_std)
+    w, wsc = quantize_mx(wf)
+    c = np.full((m + c_extra_rows, c_row_stride), C_SENTINEL, dtype=np.uint16)
+    return MxProblem(m, n, k, a_row_stride, c_row_stride, a, asc, w, wsc, c, seed)

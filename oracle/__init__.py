@@ -16,7 +16,8 @@ module doc's "Numerics" paragraph.
 
 It also holds the FP8 activation quantizer and the W8A8 GEMM it feeds
 (page "fp8_act_quant.rs": per-token groups of 128 K elements), with the
-arithmetic reading stated at their functions.
+arithmetic reading stated at their functions, and the W4A4 MX GEMV (page
+"w4a4_proj/mx_plan.rs", read as OCP MXFP4) in ``w4a4_oracle.c``.
 
 This module is argument marshalling around that C code, plus the parity
 tolerance the GPU result is graded with.
@@ -41,6 +42,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w8a16_oracle.c")
+_SRC_MX = os.path.join(_HERE, "w4a4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 K_BLOCK = 128
@@ -50,11 +52,11 @@ def build(force: bool = False) -> str:
     """Compile ``liboracle.so`` next to its source (gcc, -O2, no fast-math,
     no FMA contraction, OpenMP over output elements)."""
     if force or not os.path.exists(_LIB) or \
-            os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_MX)):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
                "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-               _SRC, "-o", tmp, "-lm"]
+               _SRC, _SRC_MX, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -99,6 +101,13 @@ def _load():
                                             u32p, u32p, ctypes.c_int64, u16p, f64p, f64p,
                                             ctypes.c_int]
         lib.oracle_w8a8_gemm_at.restype = ctypes.c_int
+        lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_w4a4_gemm.argtypes = [u8p, u32, u8p, u8p, u8p, u16p, u32, u32, u32, u32,
+                                         f64p, f64p, ctypes.c_int]
+        lib.oracle_w4a4_gemm.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -288,6 +297,54 @@ def gemm_w8a8_at(qa: np.ndarray, sa: np.ndarray, w: np.ndarray, sw: np.ndarray, 
         int(threads))
     if rc != 0:
         raise ValueError("oracle: invalid shape or sample index")
+    return c, tot, bound
+
+
+# ---------------------------------------------------------------------------
+# W4A4 MX GEMV (page "w4a4_proj/mx_plan.rs", format read as OCP MXFP4: FP4
+# E2M1 elements two per byte, even element in the low nibble, one E8M0 scale
+# per 32 K elements of a row); the arithmetic is in w4a4_oracle.c.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one FP4 E2M1 code (low 4 bits)."""
+    return _load().oracle_e2m1_value(int(code) & 0xF)
+
+
+def e8m0_value(code: int) -> float:
+    """Value of one E8M0 scale byte, 2^(code - 127) (NaN for 0xFF)."""
+    return _load().oracle_e8m0_value(int(code) & 0xFF)
+
+
+def gemm_w4a4(a: np.ndarray, a_scale: np.ndarray, w: np.ndarray, w_scale: np.ndarray,
+              m: int, n: int, k: int, a_row_stride: Optional[int] = None,
+              c_row_stride: Optional[int] = None, threads: int = 0
+              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Whole W4A4 GEMM.  ``a`` packed FP4 bytes with a row pitch of
+    ``a_row_stride`` elements (default k), ``a_scale`` E8M0 [m, k/32], ``w``
+    packed FP4 [n, k/2], ``w_scale`` E8M0 [n, k/32].  Returns (c_bits [m,
+    c_row_stride], tot [m, n], bound [m, n])."""
+    a_row_stride = k if a_row_stride is None else int(a_row_stride)
+    c_row_stride = n if c_row_stride is None else int(c_row_stride)
+    a = np.ascontiguousarray(a, dtype=np.uint8).reshape(-1)
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.uint8).reshape(-1)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.uint8).reshape(-1)
+    assert a.size >= (m - 1) * (a_row_stride // 2) + k // 2 and w.size >= n * k // 2
+    assert a_scale.size >= m * (k // MX_BLOCK) and w_scale.size >= n * (k // MX_BLOCK)
+    c = np.zeros((m, c_row_stride), dtype=np.uint16)
+    tot = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = _load().oracle_w4a4_gemm(
+        _ptr(a, ctypes.c_uint8), a_row_stride, _ptr(a_scale, ctypes.c_uint8),
+        _ptr(w, ctypes.c_uint8), _ptr(w_scale, ctypes.c_uint8), _ptr(c, ctypes.c_uint16),
+        c_row_stride, m, n, k, _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double),
+        int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid W4A4 shape m=%d n=%d k=%d" % (m, n, k))
     return c, tot, bound
 
 

@@ -662,3 +662,150 @@ def test_within_tolerance_is_elementwise():
     o = np.uint16([_bits(1.0), _bits(1.0), _bits(1.0), _bits(-3.0 - 2 ** -6)])
     b = np.float64([0.0, 1e3, 1e3, 0.0])
     assert oracle.within_tolerance(g, o, b).tolist() == [True, True, False, True]
+
+
+# ------------------------------------------------------------- W4A4 MX GEMV
+#
+# Reading of page "w4a4_proj/mx_plan.rs": OCP MXFP4 (E2M1 elements, two per
+# byte with the even element in the low nibble, one E8M0 scale per 32 K
+# elements).  Pins: the format table (tests/golden/e2m1_anchors.txt), torch's
+# float8_e8m0fnu decode, exact rationals rounded by brute force, invariants.
+
+def _e2m1_golden():
+    out = {}
+    for line in open(os.path.join(GOLDEN, "e2m1_anchors.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        out[int(code, 16)] = float(val)
+    return out
+
+
+def test_e2m1_decode_equals_the_format_table():
+    table = _e2m1_golden()
+    assert sorted(table) == list(range(16))
+    for code, val in table.items():
+        got = oracle.e2m1_value(code)
+        assert got == val and math.copysign(1.0, got) == math.copysign(1.0, val), code
+    # only the low 4 bits are read
+    assert oracle.e2m1_value(0xF2) == 1.0
+
+
+def test_e8m0_decode_equals_torch_on_all_codes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().tolist()
+    for e in range(256):
+        got = oracle.e8m0_value(e)
+        if e == 255:
+            assert math.isnan(got) and math.isnan(ref[e])
+        else:
+            assert got == ref[e] == math.ldexp(1.0, e - 127), e
+
+
+def _mx_rand(rng, m, n, k, a_pitch=None):
+    a_pitch = k if a_pitch is None else a_pitch
+    a = rng.integers(0, 256, size=(m, a_pitch // 2), dtype=np.uint8)
+    w = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    asc = rng.integers(118, 136, size=(m, k // 32), dtype=np.uint8)
+    wsc = rng.integers(118, 136, size=(n, k // 32), dtype=np.uint8)
+    return a, asc, w, wsc
+
+
+def _exact_w4a4(a, asc, w, wsc, m, n, k):
+    vals = [Fraction(v) for v in _e2m1_golden_list()]
+    out = np.empty((m, n), dtype=object)
+    for i in range(m):
+        for j in range(n):
+            tot = Fraction(0)
+            for b in range(k // 32):
+                s = Fraction(2) ** (int(asc[i, b]) - 127) * Fraction(2) ** (int(wsc[j, b]) - 127)
+                p = Fraction(0)
+                for t in range(32 * b, 32 * b + 32):
+                    ai = (int(a[i, t // 2]) >> (4 * (t % 2))) & 15
+                    wj = (int(w[j, t // 2]) >> (4 * (t % 2))) & 15
+                    p += vals[ai] * vals[wj]
+                tot += s * p
+            out[i, j] = tot
+    return out
+
+
+def _e2m1_golden_list():
+    t = _e2m1_golden()
+    return [t[c] for c in range(16)]
+
+
+@pytest.mark.parametrize("m,n,k,pad", [(1, 1, 32, 0), (2, 5, 64, 32), (3, 17, 128, 64),
+                                       (1, 3, 256, 0)])
+def test_w4a4_gemm_equals_exact_rational_then_rne(m, n, k, pad):
+    rng = np.random.default_rng(700 + m + n + k)
+    a, asc, w, wsc = _mx_rand(rng, m, n, k, k + pad)
+    c, tot, bound = oracle.gemm_w4a4(a, asc, w, wsc, m, n, k, a_row_stride=k + pad)
+    exact = _exact_w4a4(a, asc, w, wsc, m, n, k)
+    for i in range(m):
+        for j in range(n):
+            assert int(c[i, j]) == brute_bf16_rne(exact[i, j]), (i, j)
+            assert tot[i, j] == float(exact[i, j])
+
+
+def test_w4a4_pad_is_not_read():
+    rng = np.random.default_rng(11)
+    a, asc, w, wsc = _mx_rand(rng, 2, 4, 128, 192)
+    c1, t1, _ = oracle.gemm_w4a4(a, asc, w, wsc, 2, 4, 128, a_row_stride=192)
+    a[:, 64:] ^= 0xFF
+    c2, t2, _ = oracle.gemm_w4a4(a, asc, w, wsc, 2, 4, 128, a_row_stride=192)
+    assert np.array_equal(c1, c2) and np.array_equal(t1, t2)
+
+
+def test_w4a4_even_element_is_the_low_nibble():
+    k = 128
+    a = np.zeros((1, k // 2), np.uint8)
+    w = np.zeros((1, k // 2), np.uint8)
+    asc = np.full((1, k // 32), 127, np.uint8)
+    wsc = np.full((1, k // 32), 127, np.uint8)
+    a[0, 0] = 0x02                       # element 0 = 1.0, element 1 = 0
+    w[0, 0] = 0x20                       # element 0 = 0, element 1 = 1.0
+    _, tot, _ = oracle.gemm_w4a4(a, asc, w, wsc, 1, 1, k)
+    assert tot[0, 0] == 0.0
+    w[0, 0] = 0x07                       # element 0 = 6.0
+    _, tot, _ = oracle.gemm_w4a4(a, asc, w, wsc, 1, 1, k)
+    assert tot[0, 0] == 6.0
+    a[0, 1] = 0x50                       # element 3 = 3.0; w element 3 = 0
+    _, tot, _ = oracle.gemm_w4a4(a, asc, w, wsc, 1, 1, k)
+    assert tot[0, 0] == 6.0
+
+
+def test_w4a4_invariants():
+    rng = np.random.default_rng(12)
+    m, n, k = 3, 6, 256
+    a, asc, w, wsc = _mx_rand(rng, m, n, k)
+    c, tot, bound = oracle.gemm_w4a4(a, asc, w, wsc, m, n, k)
+    # zero weights
+    _, t0, b0 = oracle.gemm_w4a4(a, asc, np.zeros_like(w), wsc, m, n, k)
+    assert (t0 == 0).all() and (b0 == 0).all()
+    # negating every activation (sign bit of each nibble) negates the result
+    cn, tn, _ = oracle.gemm_w4a4(a ^ 0x88, asc, w, wsc, m, n, k)
+    assert np.array_equal(tn, -tot)
+    nz = tot != 0
+    assert np.array_equal(cn[nz] ^ 0x8000, c[nz])
+    # one block alone, then its weight scale exponent + 1: exactly twice
+    wb = np.zeros_like(w)
+    wb[:, 32:48] = w[:, 32:48]           # K block 2 (elements 64..95)
+    _, t1, _ = oracle.gemm_w4a4(a, asc, wb, wsc, m, n, k)
+    wsc2 = wsc.copy()
+    wsc2[:, 2] += 1
+    _, t2, _ = oracle.gemm_w4a4(a, asc, wb, wsc2, m, n, k)
+    assert np.array_equal(t2, 2 * t1)
+    # raising another block's scale does not change it
+    wsc3 = wsc.copy()
+    wsc3[:, 5] += 3
+    _, t3, _ = oracle.gemm_w4a4(a, asc, wb, wsc3, m, n, k)
+    assert np.array_equal(t3, t1)
+    # permuting whole 32-element blocks of A and W together with their
+    # scales leaves the total unchanged (up to the order of the block sums)
+    perm = rng.permutation(k // 32)
+    ap = a.reshape(m, k // 32, 16)[:, perm].reshape(m, k // 2)
+    wp = w.reshape(n, k // 32, 16)[:, perm].reshape(n, k // 2)
+    _, tp, _ = oracle.gemm_w4a4(ap, asc[:, perm], wp, wsc[:, perm], m, n, k)
+    assert (np.abs(tp - tot) <= bound * 2.0 ** -50).all()
+    # rows are independent
+    _, tr, _ = oracle.gemm_w4a4(a[1:2], asc[1:2], w, wsc, 1, n, k)
+    assert np.array_equal(tr[0], tot[1])
