@@ -36,6 +36,8 @@ KERNEL_STREAM = 1
 KERNEL_TILE = 2
 KERNEL_RING = 3
 KERNEL_W8A8 = 4
+KERNEL_W4A4 = 5
+KERNEL_W4A4_PS = 6
 
 FLAG_DIRECT = 1
 FLAG_A8 = 2
@@ -45,7 +47,8 @@ FLAG_XCD_LOCAL = 4
 EXPORTS = ("w8a16_check_args", "w8a16_plan", "w8a16_plan_finalize", "w8a16_gemm",
            "w8a16_gemm_planned", "w8a16_gemm_noalloc", "w8a16_plan_batched", "w8a16_gemm_batched",
            "w8a16_act_quant_fp8", "w8a16_plan_w8a8", "w8a16_gemm_w8a8",
-           "w8a16_gemm_w8a8_planned", "w8a16_status_string", "w8a16_last_error")
+           "w8a16_gemm_w8a8_planned", "w8a16_gemm_w4a4", "w8a16_plan_w4a4",
+           "w8a16_gemm_w4a4_planned", "w8a16_status_string", "w8a16_last_error")
 
 MAX_BATCH = 8
 
@@ -121,6 +124,13 @@ def library() -> ctypes.CDLL:
         lib.w8a16_gemm_w8a8_planned.argtypes = [vp, u32, vp, vp, vp, vp, u32, u32, u32, u32,
                                                 ctypes.POINTER(Plan), vp]
         lib.w8a16_gemm_w8a8_planned.restype = ctypes.c_int
+        lib.w8a16_gemm_w4a4.argtypes = [vp, u32, vp, vp, vp, vp, u32, u32, u32, u32, vp]
+        lib.w8a16_gemm_w4a4.restype = ctypes.c_int
+        lib.w8a16_plan_w4a4.argtypes = [u32, u32, u32, u32, ctypes.POINTER(Plan)]
+        lib.w8a16_plan_w4a4.restype = ctypes.c_int
+        lib.w8a16_gemm_w4a4_planned.argtypes = [vp, u32, vp, vp, vp, vp, u32, u32, u32, u32,
+                                                ctypes.POINTER(Plan), vp]
+        lib.w8a16_gemm_w4a4_planned.restype = ctypes.c_int
         lib.w8a16_status_string.argtypes = [ctypes.c_int]
         lib.w8a16_status_string.restype = ctypes.c_char_p
         lib.w8a16_last_error.argtypes = []
@@ -316,6 +326,62 @@ def gemm_w8a8_raw(qa_ptr: int, qa_row_stride: int, a_scales_ptr: int, w_ptr: int
     return int(lib.w8a16_gemm_w8a8_planned(qa_ptr, qa_row_stride, a_scales_ptr, w_ptr,
                                            scale_ptr, c_ptr, c_row_stride, m, n, k,
                                            ctypes.byref(plan_), stream))
+
+
+def plan_w4a4(m: int, n: int, k: int, cu_count: int = 0) -> Plan:
+    """Default plan of the W4A4 MX GEMV (no GPU call)."""
+    p = Plan()
+    _raise_if(library().w8a16_plan_w4a4(m, n, k, cu_count, ctypes.byref(p)))
+    return p
+
+
+def gemm_w4a4_raw(a_ptr: int, a_row_stride: int, a_scale_ptr: int, w_ptr: int,
+                  w_scale_ptr: int, c_ptr: int, c_row_stride: int, m: int, n: int, k: int,
+                  stream: int = 0, plan_: Optional[Plan] = None) -> int:
+    """Direct call of w8a16_gemm_w4a4 (or its planned form) with device
+    addresses; a_row_stride in FP4 elements.  Returns the status."""
+    lib = library()
+    if plan_ is None:
+        return int(lib.w8a16_gemm_w4a4(a_ptr, a_row_stride, a_scale_ptr, w_ptr, w_scale_ptr,
+                                       c_ptr, c_row_stride, m, n, k, stream))
+    return int(lib.w8a16_gemm_w4a4_planned(a_ptr, a_row_stride, a_scale_ptr, w_ptr,
+                                           w_scale_ptr, c_ptr, c_row_stride, m, n, k,
+                                           ctypes.byref(plan_), stream))
+
+
+def gemm_w4a4(a, a_scale, w, w_scale, k: int, c=None, *, plan_: Optional[Plan] = None,
+              stream=None):
+    """W4A4 MX GEMV on the current (or given) torch stream.
+
+    a: uint8 [m, >= k/2] packed FP4 (two E2M1 per byte, even element in the
+    low nibble), unit column stride, row stride a multiple of 16 bytes;
+    a_scale: uint8 [m, k/32] E8M0, contiguous; w: uint8 [n, k/2] packed FP4,
+    contiguous; w_scale: uint8 [n, k/32] E8M0, contiguous.  c: optional
+    bfloat16 [m, n] output with unit column stride.  Returns c."""
+    import torch
+    m, n = a.shape[0], w.shape[0]
+    for name, t in (("a", a), ("a_scale", a_scale), ("w", w), ("w_scale", w_scale)):
+        if t.dtype != torch.uint8:
+            raise ValueError("%s must be uint8 (packed FP4 or E8M0 bytes)" % name)
+    if a.stride(1) != 1 or not (w.is_contiguous() and a_scale.is_contiguous() and
+                                w_scale.is_contiguous()):
+        raise ValueError("a needs unit column stride; w and the scales must be contiguous")
+    if w.shape[1] != k // 2 or a.shape[1] < k // 2:
+        raise ValueError("w must be [n, k/2] bytes and a at least k/2 bytes wide")
+    if a_scale.shape != (m, k // 32) or w_scale.shape != (n, k // 32):
+        raise ValueError("scales must be [rows, k/32]")
+    if not (a.is_cuda and a_scale.is_cuda and w.is_cuda and w_scale.is_cuda):
+        raise ValueError("operands must be CUDA tensors")
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    elif c.dtype != torch.bfloat16 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
+        raise ValueError("c must be bfloat16 [m, n] with unit column stride")
+    stream = torch.cuda.current_stream() if stream is None else stream
+    st = gemm_w4a4_raw(a.data_ptr(), a.stride(0) * 2, a_scale.data_ptr(), w.data_ptr(),
+                       w_scale.data_ptr(), c.data_ptr(), c.stride(0), m, n, k,
+                       stream.cuda_stream, plan_)
+    _raise_if(st)
+    return c
 
 
 def act_quant_fp8(a, *, stream=None):

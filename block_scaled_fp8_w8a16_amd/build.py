@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw8a16.so")
 
 SOURCES = ["plan.cpp", "api.hip", "stream_kernel.hip", "tile_m64.hip", "tile_m128.hip",
-           "wide_kernel.hip", "split_reduce.hip", "ring_kernel.hip", "w8a8_kernel.hip"]
+           "wide_kernel.hip", "split_reduce.hip", "ring_kernel.hip", "w8a8_kernel.hip",
+           "w4a4_kernel.hip"]
 HEADERS = ["plan.h", "kernels.h", "device_common.h", "tile_kernel.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

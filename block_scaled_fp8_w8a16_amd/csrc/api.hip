@@ -441,6 +441,77 @@ int w8a16_gemm_w8a8(const void *qa, uint32_t qa_row_stride, const float *a_scale
                                    c_row_stride, m, n, k, nullptr, stream);
 }
 
+int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                            const void *w_fp4, const uint8_t *w_scale, void *c,
+                            uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
+                            const w8a16_plan_t *plan, void *stream)
+{
+    using namespace w8a16;
+    int st = check_args_w4a4(m, n, k, a_row_stride, c_row_stride);
+    if (st != W8A16_OK)
+        return st;
+    if (!a || !a_scale || !w_fp4 || !w_scale || !c)
+        return fail(W8A16_ERR_NULL_PTR,
+                    "w8a16_gemm_w4a4: a, a_scale, w_fp4, w_scale and c must be non-null");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    w8a16_plan_t p;
+    if (plan) {
+        p = *plan;
+        st = plan_finalize(m, n, k, &p);
+        if (st != W8A16_OK)
+            return st;
+        if (p.kernel != W8A16_KERNEL_W4A4 && p.kernel != W8A16_KERNEL_W4A4_PS)
+            return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_w4a4: plan kernel must be "
+                                            "W8A16_KERNEL_W4A4 or W8A16_KERNEL_W4A4_PS");
+    } else {
+        uint32_t cus = 0;
+        st = device_cu_count(dev, &cus);
+        if (st != W8A16_OK)
+            return st;
+        st = make_plan_w4a4(m, n, k, cus, &p);
+        if (st != W8A16_OK)
+            return st;
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    Workspace wsp;
+    if (p.counter_count > 0) {
+        st = get_workspace(dev, hs, p, &wsp);
+        if (st != W8A16_OK)
+            return st;
+    }
+    MxArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.a = static_cast<const uint8_t *>(a);
+    g.a_scale = a_scale;
+    g.w = static_cast<const uint8_t *>(w_fp4);
+    g.w_scale = w_scale;
+    g.c = static_cast<uint8_t *>(c);
+    g.counters = wsp.counters;
+    g.a_stride = a_row_stride / 2u;
+    g.c_stride = c_row_stride;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.m_tiles = p.m_tiles;
+    g.n_tiles = p.n_tiles;
+    e = launch_w4a4(g, p, hs);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    set_last_error("");
+    return W8A16_OK;
+}
+
+int w8a16_gemm_w4a4(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                    const void *w_fp4, const uint8_t *w_scale, void *c, uint32_t c_row_stride,
+                    uint32_t m, uint32_t n, uint32_t k, void *stream)
+{
+    return w8a16_gemm_w4a4_planned(a, a_row_stride, a_scale, w_fp4, w_scale, c, c_row_stride,
+                                   m, n, k, nullptr, stream);
+}
+
 int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream)
 {
     using namespace w8a16;

@@ -33,6 +33,19 @@ struct BatchArgs {
     uint32_t count;
 };
 
+// W4A4 MX GEMV operands: packed FP4 (two E2M1 per byte, even element in the
+// low nibble) with one E8M0 scale byte per 32 K elements of a row.
+struct MxArgs {
+    const uint8_t *a;       // FP4 [m, a_stride bytes]
+    const uint8_t *a_scale; // E8M0 [m, k/32]
+    const uint8_t *w;       // FP4 [n, k/2 bytes]
+    const uint8_t *w_scale; // E8M0 [n, k/32]
+    uint8_t *c;             // BF16 [m, c_stride]
+    uint32_t *counters;     // persistent kernel: tile ticket and exit count, zero between calls
+    uint32_t a_stride;      // A row pitch in bytes
+    uint32_t c_stride, m, n, k, m_tiles, n_tiles;
+};
+
 // FP8 activation quantizer: A BF16 [m, a_stride] -> codes [m, q_stride] and
 // scales [m, k/128].
 struct QuantArgs {
@@ -71,6 +84,7 @@ hipError_t launch_act_quant(const QuantArgs &q, hipStream_t stream);
 hipError_t launch_w8a8(const GemmArgs &g, const float *a_scales, const w8a16_plan_t &p,
                        hipStream_t stream);
 hipError_t launch_stream_batched(const BatchArgs &b, const w8a16_plan_t &p, hipStream_t stream);
+hipError_t launch_w4a4(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m64(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_tile_m128(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);
 hipError_t launch_ring(const GemmArgs &g, const w8a16_plan_t &p, hipStream_t stream);

@@ -134,6 +134,12 @@ static uint32_t w8a8_lds_bytes(uint32_t mb, uint32_t nb, uint32_t waves)
     return staging > reduce ? staging : reduce;
 }
 
+static bool w4a4_shape_supported(uint32_t mb, uint32_t nb)
+{
+    return (mb == 1 || mb == 2 || mb == 4) && (nb == 1 || nb == 2 || nb == 4) &&
+           !(mb == 4 && nb == 4);
+}
+
 static bool tile_shape_supported(uint32_t mb, uint32_t nb)
 {
     return ((mb == 4 || mb == 8) && (nb == 4 || nb == 8)) ||
@@ -296,6 +302,42 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
                      p->lds_bytes, kMaxLdsBytes);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
+    } else if (p->kernel == W8A16_KERNEL_W4A4) {
+        if (!w4a4_shape_supported(p->m_blocks, p->n_blocks) ||
+            (p->waves != 4 && p->waves != 8 && p->waves != 16) || p->flags != 0 ||
+            p->splits != 1 || m > kW4a4MaxM) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: W4A4 kernel has no (m_blocks=%u, n_blocks=%u, waves=%u, "
+                     "flags=0x%x, splits=%u) variant for m=%u (at most %u rows)", p->m_blocks,
+                     p->n_blocks, p->waves, p->flags, p->splits, m, kW4a4MaxM);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->depth = 2;
+        p->stage_steps = 0;
+        p->a_depth = 0;
+        p->block = p->waves * 64;
+        p->lds_bytes = p->waves * p->m_blocks * p->n_blocks * kAccBytes;
+    } else if (p->kernel == W8A16_KERNEL_W4A4_PS) {
+        if ((p->m_blocks != 1 && p->m_blocks != 2) || 16 * p->m_blocks < m ||
+            (p->waves != 8 && p->waves != 16) || p->flags != 0 || p->splits != 1) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: persistent W4A4 kernel needs m_blocks 1 or 2 covering m=%u, "
+                     "8 or 16 waves, no flags and no split (m_blocks=%u, waves=%u, flags=0x%x, "
+                     "splits=%u)", m, p->m_blocks, p->waves, p->flags, p->splits);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
+        p->n_blocks = 1;
+        p->depth = 4;
+        p->stage_steps = 0;
+        p->a_depth = 0;
+        p->block = p->waves * 64;
+        p->lds_bytes = w4a4_ps_lds_bytes(p->m_blocks, k);
+        if (p->lds_bytes > kMaxLdsBytes) {
+            snprintf(buf, sizeof buf,
+                     "w8a16_plan: the persistent W4A4 kernel's %u bytes of staged activations "
+                     "exceed the %u bytes of LDS", p->lds_bytes, kMaxLdsBytes);
+            return fail(W8A16_ERR_BAD_PLAN, buf);
+        }
     } else {
         snprintf(buf, sizeof buf, "w8a16_plan: unknown kernel %u", p->kernel);
         return fail(W8A16_ERR_BAD_PLAN, buf);
@@ -325,6 +367,14 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         return fail(W8A16_ERR_BAD_PLAN, buf);
     }
     p->grid = (uint32_t)grid;
+    if (p->kernel == W8A16_KERNEL_W4A4_PS) {
+        // one workgroup per CU (fewer if the weight has fewer 16-row tiles)
+        const uint32_t tiles16 = div_up(n, 16);
+        p->grid = p->cu_count < tiles16 ? p->cu_count : tiles16;
+        p->workspace_bytes = 0;
+        p->counter_count = 2;
+        return W8A16_OK;
+    }
     if (p->flags & W8A16_FLAG_XCD_LOCAL) {
         // The splits of a tile are consecutive logical workgroups, and each
         // XCD runs a contiguous range of grid / 8 of them: the ranges must
@@ -537,6 +587,84 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
                 }
             }
         }
+    }
+    st = plan_finalize(m, n, k, &p);
+    if (st != W8A16_OK)
+        return st;
+    *out = p;
+    return W8A16_OK;
+}
+
+int check_args_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
+                    uint32_t c_row_stride)
+{
+    // m, k and both pitches as the W8A16 GEMM checks them; the A pitch in
+    // FP4 elements must keep rows 16-byte aligned (a multiple of 32)
+    int st = check_args(m, n, k, a_row_stride, c_row_stride);
+    if (st == W8A16_ERR_A_STRIDE_ALIGN || (st == W8A16_OK && a_row_stride % 32 != 0)) {
+        char buf[160];
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm_w4a4: a_row_stride=%u must keep FP4 rows 16B-aligned "
+                 "(multiple of 32 elements)", a_row_stride);
+        return fail(W8A16_ERR_A_STRIDE_ALIGN, buf);
+    }
+    if (st != W8A16_OK)
+        return fail_with_name(st, "w8a16_gemm_w4a4");
+    return W8A16_OK;
+}
+
+// The page's tiers (m <= 8, 9..16, 17..32, 33..64) choose how many 16-row
+// weight tiles share each activation fragment (1, 2, 4, 2) and send 9..32
+// rows over a wide weight to the persistent entry.  Re-derived for MI355X:
+// the persistent kernel for 9..32 rows when the weight has at least 8
+// 16-row tiles per CU and A fits in LDS; otherwise the tile (16, 32 or 64
+// rows by 16, 32 or 64 columns) whose rounds of tiles ask each CU for the
+// fewest FP4 bytes of A and weight rows per K (the W8A16 stream planner's
+// rule), ties to fewer blocks per tile.  No K split.
+int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    if (!out)
+        return fail(W8A16_ERR_NULL_PTR, "w8a16_plan: null plan");
+    int st = check_args_w4a4(m, n, k, k, n);
+    if (st != W8A16_OK)
+        return st;
+    char buf[128];
+    if (m > kW4a4MaxM) {
+        snprintf(buf, sizeof buf, "w8a16_gemm_w4a4: m=%u exceeds the W4A4 tiers' %u rows", m,
+                 kW4a4MaxM);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
+    w8a16_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.cu_count = cu_count ? cu_count : kDefaultCUs;
+    p.splits = 1;
+    const uint32_t ksteps = k / kKStep;
+    const uint32_t n16 = div_up(n, 16);
+    if (m > 8 && m <= 32 && n16 >= kW4a4PsMinTilesPerCu * p.cu_count &&
+        w4a4_ps_lds_bytes(div_up(m, 16), k) <= kMaxLdsBytes) {
+        p.kernel = W8A16_KERNEL_W4A4_PS;
+        p.m_blocks = div_up(m, 16);
+        p.n_blocks = 1;
+        p.waves = 16;
+    } else {
+        p.kernel = W8A16_KERNEL_W4A4;
+        uint64_t best = ~0ull;
+        const uint32_t opts[3] = {1, 2, 4};
+        for (uint32_t mb : opts)
+            for (uint32_t nb : opts) {
+                if (!w4a4_shape_supported(mb, nb))
+                    continue;
+                const uint64_t tiles = (uint64_t)div_up(m, 16 * mb) * div_up(n16, nb);
+                const uint64_t cost = (tiles + p.cu_count - 1) / p.cu_count * (mb + nb);
+                if (cost < best || (cost == best && mb * nb < p.m_blocks * p.n_blocks)) {
+                    best = cost;
+                    p.m_blocks = mb;
+                    p.n_blocks = nb;
+                }
+            }
+        p.waves = p.m_blocks * p.n_blocks <= 2 ? 16 : 8;
+        while (p.waves > 4 && ksteps < 2 * p.waves)
+            p.waves /= 2;
     }
     st = plan_finalize(m, n, k, &p);
     if (st != W8A16_OK)
@@ -780,6 +908,11 @@ extern "C" {
 int w8a16_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
 {
     return w8a16::make_plan_w8a8(m, n, k, cu_count, out);
+}
+
+int w8a16_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
+{
+    return w8a16::make_plan_w4a4(m, n, k, cu_count, out);
 }
 
 int w8a16_plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_count,

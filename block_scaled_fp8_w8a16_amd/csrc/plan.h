@@ -127,8 +127,22 @@ constexpr bool ring_shape_ok(uint32_t mb, uint32_t nbw, uint32_t sk, uint32_t ns
            waves * mb * 1024 <= ring;
 }
 
+// W4A4 MX GEMV: most rows, and the LDS of the persistent kernel (A rows
+// padded by 16 bytes, then their scale bytes).
+constexpr uint32_t kW4a4MaxM = 64;
+constexpr uint32_t w4a4_ps_lds_bytes(uint32_t m_blocks, uint32_t k)
+{
+    return m_blocks * 16 * (k / 2 + 16) + m_blocks * 16 * (k / 32);
+}
+// The persistent kernel runs when the weight has at least this many 16-row
+// tiles per CU.
+constexpr uint32_t kW4a4PsMinTilesPerCu = 8;
+
 int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
                uint32_t c_row_stride);
+int check_args_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
+                    uint32_t c_row_stride);
+int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);
 int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);
 int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p);
 int make_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out);

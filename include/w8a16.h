@@ -90,7 +90,16 @@ typedef enum w8a16_kernel {
     /* W8A8 kernel (w8a16_gemm_w8a8 only): A given as FP8 codes with one
      * scale per (row, K step); the stream kernel's organisation with A
      * staged like the weight and one FP8 MFMA per K step.  No K split. */
-    W8A16_KERNEL_W8A8 = 4
+    W8A16_KERNEL_W8A8 = 4,
+    /* W4A4 MX kernel (w8a16_gemm_w4a4 only): a workgroup owns n_blocks
+     * 16-column blocks and m_blocks 16-row blocks of C over all of K, its
+     * waves take interleaved 128-wide K steps with one scaled FP4 MFMA per
+     * block and step, each activation fragment feeding the n_blocks weight
+     * blocks.  No K split. */
+    W8A16_KERNEL_W4A4 = 5,
+    /* Persistent W4A4 MX kernel: one workgroup per CU stages all of A in
+     * LDS, its waves pull 16-row weight tiles from a counter. */
+    W8A16_KERNEL_W4A4_PS = 6
 } w8a16_kernel;
 
 /* Launch plan.  w8a16_plan() fills every field; callers may change
@@ -283,6 +292,48 @@ int w8a16_gemm_w8a8(const void *qa, uint32_t qa_row_stride, const float *a_scale
  * m_blocks, n_blocks and waves taken from it).  For tests and tuning. */
 int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float *a_scales,
                             const void *w_fp8, const float *block_scale, void *c,
+                            uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
+                            const w8a16_plan_t *plan, void *stream);
+
+/* ---- W4A4 MX projection GEMV ---------------------------------------------
+ * The m-row W4A4 projection of page "w4a4_proj/mx_plan.rs" (up to 64 rows;
+ * weight rows in 16-row tiles; tiers by m; activation reuse across weight
+ * tiles; a persistent entry for wide weights).  The page states no number
+ * format; the reading is OCP MXFP4 for both operands: FP4 E2M1 elements
+ * (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives), two per byte with the
+ * even element in the low nibble, and one E8M0 scale byte (2^(e - 127)) per
+ * 32 consecutive K elements of a row:
+ *
+ *   C[i][j] = bf16( sum_b 2^(ea[i][b]-127) * 2^(ew[j][b]-127) * sum_{t<32} a[i][32b+t] * w[j][32b+t] )
+ *
+ *   a        FP4   [m, a_row_stride]  elements; a row is a_row_stride / 2 bytes
+ *   a_scale  E8M0  [m, k/32]          row-major, contiguous
+ *   w_fp4    FP4   [n, k]             row-major, contiguous (k/2 bytes per row)
+ *   w_scale  E8M0  [n, k/32]          row-major, contiguous
+ *   c        BF16  [m, c_row_stride]  first n elements of each row written
+ *
+ * Products are exact, sums FP32 (the matrix cores apply the two block scales
+ * to each 32-element partial), one round-to-nearest-even to BF16.  Device
+ * pointers owned by the caller.  Errors, in order: m == 0; k not a positive
+ * multiple of 128; a_row_stride < k or c_row_stride < n; a_row_stride not a
+ * multiple of 32 (16-byte rows); n == 0; a null pointer; m above 64
+ * (W8A16_ERR_BAD_PLAN).  The persistent plan uses the (device, stream)
+ * workspace's counters (see Ownership).  Asynchronous. */
+int w8a16_gemm_w4a4(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                    const void *w_fp4, const uint8_t *w_scale, void *c, uint32_t c_row_stride,
+                    uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* Default plan of the W4A4 GEMV (kernel W8A16_KERNEL_W4A4 or _W4A4_PS).
+ * Pure: no GPU call. */
+int w8a16_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count,
+                    w8a16_plan_t *out);
+
+/* w8a16_gemm_w4a4 with an explicit plan (kernel W8A16_KERNEL_W4A4:
+ * m_blocks 1, 2 or 4, n_blocks 1, 2 or 4, waves 4, 8 or 16; kernel
+ * W8A16_KERNEL_W4A4_PS: m_blocks 1 or 2 covering m, waves 8 or 16).  For
+ * tests and tuning. */
+int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                            const void *w_fp4, const uint8_t *w_scale, void *c,
                             uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
                             const w8a16_plan_t *plan, void *stream);
 

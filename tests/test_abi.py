@@ -529,3 +529,66 @@ def test_w8a8_plans():
         w8.make_plan(32, 256, 4096, w8.KERNEL_W8A8, 2, 2, 2, waves=8)
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(32, 256, 4096, w8.KERNEL_W8A8, 4, 4, 1, waves=8)
+
+
+# --------------------------------------------------------------- W4A4 MX GEMV
+
+def _w4a4_cost(m, n, mb, nb, cus=256):
+    tiles = -(-m // (16 * mb)) * -(-n // (16 * nb))
+    return -(-tiles // cus) * (mb + nb)
+
+
+W4A4_TILES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
+
+
+def test_w4a4_plans_cover_and_take_the_cheapest_tile():
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        m = int(rng.integers(1, 65))
+        n = int(rng.integers(1, 40000))
+        k = 128 * int(rng.integers(1, 65))
+        p = w8.plan_w4a4(m, n, k)
+        if p.kernel == w8.KERNEL_W4A4_PS:
+            assert 8 < m <= 32 and -(-n // 16) >= 8 * 256
+            assert p.grid == 256 and p.counter_count == 2 and p.n_blocks == 1
+            assert 16 * p.m_blocks >= m and p.lds_bytes <= 160 * 1024
+            continue
+        assert p.kernel == w8.KERNEL_W4A4 and p.splits == 1
+        assert p.m_tiles * 16 * p.m_blocks >= m and p.n_tiles * 16 * p.n_blocks >= n
+        assert p.grid == p.m_tiles * p.n_tiles
+        best = min(_w4a4_cost(m, n, mb, nb) for mb, nb in W4A4_TILES)
+        assert _w4a4_cost(m, n, p.m_blocks, p.n_blocks) == best, (m, n, k)
+        assert p.lds_bytes == p.waves * p.m_blocks * p.n_blocks * 1024
+
+
+def test_w4a4_persistent_rule():
+    # 9..32 rows over at least 8 16-row tiles per CU
+    assert w8.plan_w4a4(16, 32768, 4096).kernel == w8.KERNEL_W4A4_PS
+    assert w8.plan_w4a4(32, 32768, 8192).kernel == w8.KERNEL_W4A4_PS
+    assert w8.plan_w4a4(8, 32768, 4096).kernel == w8.KERNEL_W4A4        # m <= 8
+    assert w8.plan_w4a4(33, 32768, 4096).kernel == w8.KERNEL_W4A4       # m > 32
+    assert w8.plan_w4a4(16, 32752, 4096).kernel == w8.KERNEL_W4A4       # 2047 tiles
+    # A must fit in LDS: 32 rows x 16384 K do not
+    assert w8.plan_w4a4(32, 65536, 16384).kernel == w8.KERNEL_W4A4
+    p = w8.plan_w4a4(12, 40000, 2048, cu_count=100)
+    assert p.kernel == w8.KERNEL_W4A4_PS and p.grid == 100
+
+
+def test_w4a4_plan_errors():
+    with pytest.raises(w8.W8A16Error) as e:
+        w8.plan_w4a4(65, 4096, 4096)
+    assert e.value.status == w8.ERR_BAD_PLAN
+    for args, status in [((0, 16, 128), w8.ERR_M_ZERO), ((1, 16, 100), w8.ERR_K_NOT_MULT_128),
+                         ((1, 0, 128), w8.ERR_N_ZERO)]:
+        with pytest.raises(w8.W8A16Error) as e:
+            w8.plan_w4a4(*args)
+        assert e.value.status == status
+    # explicit plans: unsupported tile, waves, persistent rows not covered
+    for kern, mb, nb, waves, m in [(w8.KERNEL_W4A4, 4, 4, 8, 64), (w8.KERNEL_W4A4, 1, 8, 8, 16),
+                                   (w8.KERNEL_W4A4, 1, 1, 6, 16),
+                                   (w8.KERNEL_W4A4_PS, 1, 1, 16, 17),
+                                   (w8.KERNEL_W4A4_PS, 2, 1, 4, 32)]:
+        with pytest.raises(w8.W8A16Error):
+            w8.make_plan(m, 4096, 4096, kern, mb, nb, 1, waves=waves)
+    p = w8.make_plan(17, 4096, 4096, w8.KERNEL_W4A4_PS, 2, 1, 1, waves=8, cu_count=4)
+    assert (p.grid, p.block, p.counter_count) == (4, 512, 2)
