@@ -20,6 +20,7 @@ Prints one JSON line.  Usage:
     python bench.py --m-sweep N K          (default plan for m = 1..256, one line each)
     python bench.py --batched              (Q/K/V arms in one batched call vs three calls)
     python bench.py --w8a8                 (FP8 activation quantizer + W8A8 GEMM)
+    python bench.py --w4a4                 (W4A4 MX GEMV, tiled and persistent)
     python bench.py --trace-run WORKLOAD [K]   (the timed region alone, for rocprofv3)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR WORKLOAD   (writes profiles/)
     python bench.py --summarize-trace TRACE_DIR WORKLOAD [K]          (writes profiles/)
@@ -633,6 +634,111 @@ def batched_bench(m: int = 8, k: int = 4096, steps: int = 100, warmup: int = 10)
         "kernel_source_hash": kernel_source_hash(), "note": NOTE}), flush=True)
 
 
+def time_graph(torch, stream, call, steps: int, warmup: int, scrub=None):
+    """(graph ms per call, eager ms per call) of call(0..steps-1) on
+    `stream`, with the spin-up and cache scrub of time_workload before each
+    timed region."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                call(i)
+
+        def spin_up():
+            t0 = time.perf_counter()
+            while True:
+                graph.replay()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= SPIN_UP_S:
+                    break
+            if scrub is not None:
+                scrub.run()
+
+        spin_up()
+        start.record(stream)
+        for i in range(steps):
+            call(i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = start.elapsed_time(stop) / steps
+        spin_up()
+        start.record(stream)
+        graph.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, eager_ms
+
+
+# (m, n, k, A row pitch in elements): the W8A16 workloads' shapes, and a
+# wide weight (2048 16-row tiles) that the persistent kernel serves.
+W4A4_WORKLOADS = [(8, 4096, 4096, 4096), (16, 12288, 5120, 5120), (32, 6144, 2048, 2560),
+                  (16, 32768, 4096, 4096)]
+
+
+def w4a4_bench(steps: int = 100, warmup: int = 10):
+    """The W4A4 MX GEMV on its workloads, cold (replicas over >= 512 MiB,
+    cache scrub, graph replay).  One JSON line per workload."""
+    import numpy as np
+    import torch
+    import block_scaled_fp8_w8a16_amd as w8
+    import datagen
+    w8.library()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    scrub = Scrub(torch)
+    for m, n, k, pitch in W4A4_WORKLOADS:
+        p = datagen.make_mx_problem(m, n, k, seed=9000 + m + n + k, a_row_stride=pitch)
+        per = p.a.nbytes + p.a_scale.nbytes + p.w.nbytes + p.w_scale.nbytes + 2 * m * n
+        reps = max(1, -(-ARENA_BYTES // per))
+        dev = torch.device("cuda")
+
+        def rep(x):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev).reshape(1, -1).repeat(reps, 1)
+
+        a, asc, w, wsc = rep(p.a), rep(p.a_scale), rep(p.w), rep(p.w_scale)
+        c = torch.zeros((reps, m * n), dtype=torch.int16, device=dev)
+        stream = torch.cuda.Stream()
+
+        def call(i):
+            r = i % reps
+            st = w8.gemm_w4a4_raw(a[r].data_ptr(), pitch, asc[r].data_ptr(), w[r].data_ptr(),
+                                  wsc[r].data_ptr(), c[r].data_ptr(), n, m, n, k,
+                                  stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(w8.last_error())
+
+        ms, eager = time_graph(torch, stream, call, steps, warmup, scrub)
+        ok = True
+        for r in range(min(reps, steps)):
+            cc = c[r].cpu().numpy().view(np.uint16)
+            ok &= bool(((cc & 0x7F80) != 0x7F80).all())
+        nbytes = p.algorithmic_bytes()
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        plan = w8.plan_w4a4(m, n, k, cus)
+        kname = "w8a16_w4a4_ps_kernel" if plan.kernel == w8.KERNEL_W4A4_PS else "w8a16_w4a4_kernel"
+        print(json.dumps({
+            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+            "config": {"workload": "w4a4_m%d_n%d_k%d" % (m, n, k), "m": m, "n": n, "k": k,
+                       "a_row_stride": pitch, "format": "MXFP4 (E2M1, E8M0 per 32)",
+                       "weights": "cold", "arena_replicas": reps},
+            "us_per_call": round(ms * 1e3, 3), "us_per_call_eager": round(eager * 1e3, 3),
+            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 3),
+            "plan": plan.as_dict(), "output_sane": ok,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": kname, "algorithmic_bytes_per_launch": nbytes},
+            "kernel_source_hash": kernel_source_hash(), "note": NOTE}), flush=True)
+        del a, asc, w, wsc, c
+        torch.cuda.empty_cache()
+
+
 W8A8_WORKLOADS = ["m8_n4096_k4096", "m16_n12288_k5120", "m32_n6144_k2048_strided"]
 
 
@@ -733,6 +839,9 @@ def w8a8_bench(steps: int = 100, warmup: int = 10):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--w4a4":
+        w4a4_bench()
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--w8a8":
         w8a8_bench()
         return

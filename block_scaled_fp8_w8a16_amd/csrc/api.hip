@@ -476,12 +476,6 @@ int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t 
             return st;
     }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    Workspace wsp;
-    if (p.counter_count > 0) {
-        st = get_workspace(dev, hs, p, &wsp);
-        if (st != W8A16_OK)
-            return st;
-    }
     MxArgs g;
     std::memset(&g, 0, sizeof g);
     g.a = static_cast<const uint8_t *>(a);
@@ -489,7 +483,6 @@ int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t 
     g.w = static_cast<const uint8_t *>(w_fp4);
     g.w_scale = w_scale;
     g.c = static_cast<uint8_t *>(c);
-    g.counters = wsp.counters;
     g.a_stride = a_row_stride / 2u;
     g.c_stride = c_row_stride;
     g.m = m;
@@ -497,6 +490,8 @@ int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t 
     g.k = k;
     g.m_tiles = p.m_tiles;
     g.n_tiles = p.n_tiles;
+    g.tiles_base = (n + 15u) / 16u / p.grid;
+    g.tiles_extra = (n + 15u) / 16u % p.grid;
     e = launch_w4a4(g, p, hs);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");

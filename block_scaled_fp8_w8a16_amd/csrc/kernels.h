@@ -41,9 +41,11 @@ struct MxArgs {
     const uint8_t *w;       // FP4 [n, k/2 bytes]
     const uint8_t *w_scale; // E8M0 [n, k/32]
     uint8_t *c;             // BF16 [m, c_stride]
-    uint32_t *counters;     // persistent kernel: tile ticket and exit count, zero between calls
     uint32_t a_stride;      // A row pitch in bytes
     uint32_t c_stride, m, n, k, m_tiles, n_tiles;
+    // persistent kernel: workgroup g owns tiles_base + (g < tiles_extra)
+    // 16-row weight tiles, starting at g * tiles_base + min(g, tiles_extra)
+    uint32_t tiles_base, tiles_extra;
 };
 
 // FP8 activation quantizer: A BF16 [m, a_stride] -> codes [m, q_stride] and

@@ -304,7 +304,7 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         }
     } else if (p->kernel == W8A16_KERNEL_W4A4) {
         if (!w4a4_shape_supported(p->m_blocks, p->n_blocks) ||
-            (p->waves != 4 && p->waves != 8 && p->waves != 16) || p->flags != 0 ||
+            !w4a4_variant_ok(p->m_blocks, p->n_blocks, p->waves) || p->flags != 0 ||
             p->splits != 1 || m > kW4a4MaxM) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: W4A4 kernel has no (m_blocks=%u, n_blocks=%u, waves=%u, "
@@ -318,24 +318,26 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
         p->block = p->waves * 64;
         p->lds_bytes = p->waves * p->m_blocks * p->n_blocks * kAccBytes;
     } else if (p->kernel == W8A16_KERNEL_W4A4_PS) {
-        if ((p->m_blocks != 1 && p->m_blocks != 2) || 16 * p->m_blocks < m ||
-            (p->waves != 8 && p->waves != 16) || p->flags != 0 || p->splits != 1) {
+        if ((p->m_blocks != 1 && p->m_blocks != 2 && p->m_blocks != 4) || 16 * p->m_blocks < m ||
+            (p->waves != 4 && p->waves != 8 && p->waves != 16) || p->flags != 0 ||
+            p->splits != 1 || m > kW4a4MaxM) {
             snprintf(buf, sizeof buf,
-                     "w8a16_plan: persistent W4A4 kernel needs m_blocks 1 or 2 covering m=%u, "
-                     "8 or 16 waves, no flags and no split (m_blocks=%u, waves=%u, flags=0x%x, "
-                     "splits=%u)", m, p->m_blocks, p->waves, p->flags, p->splits);
+                     "w8a16_plan: persistent W4A4 kernel needs m_blocks 1, 2 or 4 covering "
+                     "m=%u (at most %u rows), 4, 8 or 16 waves, no flags and no split "
+                     "(m_blocks=%u, waves=%u, flags=0x%x, splits=%u)", m, kW4a4MaxM,
+                     p->m_blocks, p->waves, p->flags, p->splits);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
         p->n_blocks = 1;
-        p->depth = 4;
+        p->depth = 3;
         p->stage_steps = 0;
         p->a_depth = 0;
         p->block = p->waves * 64;
-        p->lds_bytes = w4a4_ps_lds_bytes(p->m_blocks, k);
+        p->lds_bytes = w4a4_ps_lds_bytes(p->m_blocks, k, p->waves);
         if (p->lds_bytes > kMaxLdsBytes) {
             snprintf(buf, sizeof buf,
                      "w8a16_plan: the persistent W4A4 kernel's %u bytes of staged activations "
-                     "exceed the %u bytes of LDS", p->lds_bytes, kMaxLdsBytes);
+                     "and partial tiles exceed the %u bytes of LDS", p->lds_bytes, kMaxLdsBytes);
             return fail(W8A16_ERR_BAD_PLAN, buf);
         }
     } else {
@@ -368,11 +370,12 @@ int plan_finalize(uint32_t m, uint32_t n, uint32_t k, w8a16_plan_t *p)
     }
     p->grid = (uint32_t)grid;
     if (p->kernel == W8A16_KERNEL_W4A4_PS) {
-        // one workgroup per CU (fewer if the weight has fewer 16-row tiles)
+        // one workgroup per CU, each with an equal share of the 16-row
+        // weight tiles (fewer workgroups than CUs for fewer tiles)
         const uint32_t tiles16 = div_up(n, 16);
         p->grid = p->cu_count < tiles16 ? p->cu_count : tiles16;
         p->workspace_bytes = 0;
-        p->counter_count = 2;
+        p->counter_count = 0;
         return W8A16_OK;
     }
     if (p->flags & W8A16_FLAG_XCD_LOCAL) {
@@ -610,17 +613,30 @@ int check_args_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
     }
     if (st != W8A16_OK)
         return fail_with_name(st, "w8a16_gemm_w4a4");
+    // the kernels address a tile's rows (at most 64) through 32-bit buffer
+    // ranges below 2^31 bytes
+    if (k > kW4a4MaxK || a_row_stride > kW4a4MaxK) {
+        char buf[160];
+        snprintf(buf, sizeof buf,
+                 "w8a16_gemm_w4a4: k=%u and a_row_stride=%u must be at most %u elements", k,
+                 a_row_stride, kW4a4MaxK);
+        return fail(W8A16_ERR_BAD_PLAN, buf);
+    }
     return W8A16_OK;
 }
 
 // The page's tiers (m <= 8, 9..16, 17..32, 33..64) choose how many 16-row
 // weight tiles share each activation fragment (1, 2, 4, 2) and send 9..32
-// rows over a wide weight to the persistent entry.  Re-derived for MI355X:
-// the persistent kernel for 9..32 rows when the weight has at least 8
-// 16-row tiles per CU and A fits in LDS; otherwise the tile (16, 32 or 64
-// rows by 16, 32 or 64 columns) whose rounds of tiles ask each CU for the
-// fewest FP4 bytes of A and weight rows per K (the W8A16 stream planner's
-// rule), ties to fewer blocks per tile.  No K split.
+// rows over a wide weight to the persistent entry.  Re-derived for MI355X,
+// where a CU streams at most about 20 KiB/us from HBM, so every CU must get
+// an equal share of the weight and A must not be re-read per tile: the
+// persistent kernel (A once per CU in LDS, equal contiguous tile ranges per
+// CU, K split over the waves) when the weight has two or more 16-row tiles
+// per CU and A fits in LDS; otherwise (a weight of one tile per CU or so is
+// read in one round trip, and the tiled kernel starts it sooner) the tile
+// (16, 32 or 64 rows by 16, 32 or 64 columns) whose rounds of tiles ask
+// each CU for the fewest FP4 bytes of A and weight rows per K (the W8A16
+// stream planner's rule), ties to fewer blocks per tile.
 int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_t *out)
 {
     if (!out)
@@ -640,12 +656,22 @@ int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
     p.splits = 1;
     const uint32_t ksteps = k / kKStep;
     const uint32_t n16 = div_up(n, 16);
-    if (m > 8 && m <= 32 && n16 >= kW4a4PsMinTilesPerCu * p.cu_count &&
-        w4a4_ps_lds_bytes(div_up(m, 16), k) <= kMaxLdsBytes) {
+    // persistent kernel when the weight has at least kW4a4PsMinTilesPerCu
+    // 16-row tiles per CU and A fits in LDS: 8 waves (measured ahead of 16
+    // on MI355X), 4 when the workgroup has fewer items (tiles x groups of 4
+    // K steps) or LDS room
+    const uint32_t ps_mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    const uint32_t ps_grid = p.cu_count < n16 ? p.cu_count : n16;
+    const uint64_t ps_items = (uint64_t)div_up(n16, ps_grid) * div_up(ksteps, 4);
+    uint32_t ps_waves = 8;
+    if (w4a4_ps_lds_bytes(ps_mb, k, ps_waves) > kMaxLdsBytes || ps_items < ps_waves)
+        ps_waves = 4;
+    if (n16 >= kW4a4PsMinTilesPerCu * p.cu_count &&
+        w4a4_ps_lds_bytes(ps_mb, k, ps_waves) <= kMaxLdsBytes) {
         p.kernel = W8A16_KERNEL_W4A4_PS;
-        p.m_blocks = div_up(m, 16);
+        p.m_blocks = ps_mb;
         p.n_blocks = 1;
-        p.waves = 16;
+        p.waves = ps_waves;
     } else {
         p.kernel = W8A16_KERNEL_W4A4;
         uint64_t best = ~0ull;
@@ -662,8 +688,12 @@ int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
                     p.n_blocks = nb;
                 }
             }
-        p.waves = p.m_blocks * p.n_blocks <= 2 ? 16 : 8;
-        while (p.waves > 4 && ksteps < 2 * p.waves)
+        // the most waves whose registers hold two groups of 4 steps, fewer
+        // until every wave has two groups
+        p.waves = w4a4_variant_ok(p.m_blocks, p.n_blocks, 16) ? 16
+                  : (w4a4_variant_ok(p.m_blocks, p.n_blocks, 8) ? 8 : 4);
+        const uint32_t groups = div_up(ksteps, 4);
+        while (p.waves > 4 && groups < 2 * p.waves)
             p.waves /= 2;
     }
     st = plan_finalize(m, n, k, &p);

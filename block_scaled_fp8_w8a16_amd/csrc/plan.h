@@ -127,16 +127,34 @@ constexpr bool ring_shape_ok(uint32_t mb, uint32_t nbw, uint32_t sk, uint32_t ns
            waves * mb * 1024 <= ring;
 }
 
-// W4A4 MX GEMV: most rows, and the LDS of the persistent kernel (A rows
-// padded by 16 bytes, then their scale bytes).
+// W4A4 MX GEMV: most rows and largest K.  LDS of the persistent kernel: A
+// (16 m_blocks rows padded by 16 bytes), its scale bytes (rounded up to
+// 256) and two partial 16 x 16 tiles per wave and row block.
 constexpr uint32_t kW4a4MaxM = 64;
-constexpr uint32_t w4a4_ps_lds_bytes(uint32_t m_blocks, uint32_t k)
+constexpr uint32_t kW4a4MaxK = 1u << 24;          // K and A pitch, in FP4 elements
+constexpr uint32_t w4a4_ps_a_bytes(uint32_t m_blocks, uint32_t k)
 {
-    return m_blocks * 16 * (k / 2 + 16) + m_blocks * 16 * (k / 32);
+    return m_blocks * 16 * (k / 2 + 16);
 }
-// The persistent kernel runs when the weight has at least this many 16-row
+constexpr uint32_t w4a4_ps_s_bytes(uint32_t m_blocks, uint32_t k)
+{
+    return (m_blocks * 16 * (k / 32) + 255) / 256 * 256;
+}
+constexpr uint32_t w4a4_ps_lds_bytes(uint32_t m_blocks, uint32_t k, uint32_t waves)
+{
+    return w4a4_ps_a_bytes(m_blocks, k) + w4a4_ps_s_bytes(m_blocks, k) + waves * 2 * m_blocks * 1024;
+}
+// The persistent kernel is planned for weights of at least this many 16-row
 // tiles per CU.
-constexpr uint32_t kW4a4PsMinTilesPerCu = 8;
+constexpr uint32_t kW4a4PsMinTilesPerCu = 2;
+// Tiled W4A4 variants that are built: a wave holds two groups of 4 K steps
+// of its mb + nb operand blocks in registers, which fits the 128 VGPRs of a
+// 16-wave workgroup for one block each and the 256 of an 8-wave workgroup
+// for up to four blocks; 4 waves take any shape.
+constexpr bool w4a4_variant_ok(uint32_t mb, uint32_t nb, uint32_t waves)
+{
+    return waves == 4 || (waves == 8 && mb + nb <= 4) || (waves == 16 && mb + nb <= 2);
+}
 
 int check_args(uint32_t m, uint32_t n, uint32_t k, uint32_t a_row_stride,
                uint32_t c_row_stride);

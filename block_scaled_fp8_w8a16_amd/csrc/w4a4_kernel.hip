@@ -21,17 +21,20 @@
 //     MX block, so its scale byte is that lane's own.  A direct load in this
 //     layout reads 16 rows x 64 contiguous bytes per instruction, the whole
 //     step of each row, so the weight goes straight to registers (no LDS).
+//   * K is walked in groups of 4 steps: a lane's scale bytes for 4 steps of
+//     one row are 16 contiguous bytes, one load per group (one dword per
+//     step when K is not a multiple of 512).
 //   * Tiled kernel: a workgroup owns NBW 16-column blocks of C and MB 16-row
-//     blocks over all of K; its waves take interleaved K steps, DEPTH steps
-//     of loads in flight each; every A fragment feeds the NBW weight blocks
-//     from registers.  The waves' partial tiles are added in LDS in wave
-//     order, then stored as BF16.
+//     blocks over all of K; its waves take interleaved groups, the next
+//     group's loads in flight while one is computed; every A fragment feeds
+//     the NBW weight blocks from registers; rows of A past m are not loaded.
+//     The waves' partial tiles are added in LDS in wave order, then stored
+//     as BF16.
 //   * Persistent kernel (9..32 rows over a wide weight): one workgroup per
-//     CU stages all of A and its scales in LDS once; each wave pulls 16-row
-//     weight tiles from a counter and walks all of K for its tile alone, so
-//     A is read from HBM/L2 once per CU instead of once per tile.  Every
-//     wave stops at the first ticket past the last tile; the last workgroup
-//     to finish puts the counters back to zero for the next call.
+//     CU stages all of A and its scales in LDS once; then each wave walks
+//     its own 16-row weight tiles over all of K, taking A from LDS.  A is
+//     read once per CU instead of once per tile.  Tiles are dealt out
+//     round-robin (they all cost the same), so there is no tile counter.
 //   * Rows past m and columns past n read clamped, valid addresses and are
 //     never stored.
 
@@ -105,7 +108,90 @@ __device__ __forceinline__ void reduce_store(const MxArgs &g, f32x4_t (&acc)[NBW
     }
 }
 
-template <int MB, int NBW, int WAVES, int DEPTH, bool NTW>
+// Buffer resources.  Every global load of these kernels is a raw buffer
+// load through a resource that spans exactly the rows it may read: an
+// offset at or past the resource's byte count returns zeros without a
+// memory access.  Steps past K, rows past m or n and the prefetch past a
+// wave's last group are such offsets, so the loads need no branches and the
+// compiler's wait counts stay exact (a load under a branch makes it wait for
+// every load in flight).
+constexpr int kRsrcWord3 = 0x00020000;     // raw 32-bit data format, no swizzle
+constexpr uint32_t kOob = 0x80000000u;     // past every resource (each < 2^31 bytes)
+constexpr int kCacheNt = 2;                // nontemporal hint of a load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? kCacheNt : 0));
+}
+
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// Scale dwords of the 4 K steps of group `gidx` for one row (`row_off` =
+// the row's first scale byte in the resource): dword e holds the 4 block
+// scales of step 4 gidx + e.  SC16 (K a multiple of 512, every group
+// whole): one 16-byte load.  Otherwise one dword per step.  Steps at or
+// past `ksteps` read zeros.
+template <bool SC16>
+__device__ __forceinline__ void load_scales(uint32_t (&d)[4], __amdgpu_buffer_rsrc_t r,
+                                            uint32_t row_off, uint32_t gidx, uint32_t ksteps)
+{
+    if constexpr (SC16) {
+        const u32x4_t v = load16<false>(r, row_off + (4u * gidx < ksteps ? 16u * gidx : kOob));
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t t = 4u * gidx + e;
+            d[e] = load4(r, row_off + (t < ksteps ? 4u * t : kOob));
+        }
+    }
+}
+
+// Byte offset of step t inside a row (16 gq added per lane), or past the
+// resource for a step at or past ksteps.
+__device__ __forceinline__ uint32_t step_off(uint32_t t, uint32_t ksteps)
+{
+    return t < ksteps ? 64u * t : kOob;
+}
+
+// The byte of lane group gq (its 32-element block) of a step's scale dword.
+__device__ __forceinline__ uint32_t scale_byte(uint32_t d, uint32_t gq)
+{
+    return (d >> (8u * gq)) & 0xffu;
+}
+
+// One group of 4 K steps of a wave: weight and A fragments and scales.
+template <int MB, int NBW>
+struct MxGroup {
+    u32x4_t w[4][NBW];
+    u32x4_t a[4][MB];
+    uint32_t ws[NBW][4];
+    uint32_t as[MB][4];
+};
+
+// Groups of 4 K steps in flight per wave (the one being computed included).
+constexpr int kTileBufs = 2;
+constexpr int kPsBufs = 3;
+// Persistent kernel: A chunks (16 bytes) and scale dwords staged per
+// thread and batch.
+constexpr uint32_t kStageA = 4;
+constexpr uint32_t kStageS = 2;
+
+template <int MB, int NBW, int WAVES, bool NTW, bool SC16>
 __global__ __launch_bounds__(WAVES * 64) void w8a16_w4a4_kernel(MxArgs g)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -115,31 +201,38 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_w4a4_kernel(MxArgs g)
     const uint32_t n0 = (tile / g.m_tiles) * (NBW * 16);
     const uint32_t ksteps = g.k / 128u;
     const uint32_t kb = g.k / 32u;                     // scale bytes per row
+    const uint32_t groups = (ksteps + 3u) / 4u;
     const uint32_t rr = lane & 15u, gq = lane >> 4;
-    // this wave's K steps: wave, wave + WAVES, ... (nw of them), walked from
-    // a per-tile rotation so that neighbouring tiles read different K
-    const uint32_t nw = wave < ksteps ? (ksteps - wave + WAVES - 1) / WAVES : 0u;
-    const uint32_t rot = (tile * kRotStride) % ksteps;
-    auto phys = [&](uint32_t i) {
-        uint32_t x = wave + WAVES * i + rot;
-        return x >= ksteps ? x - ksteps : x;
+    // this wave's groups of 4 K steps: wave, wave + WAVES, ... (ng of them),
+    // walked from a per-tile rotation so that neighbouring tiles read
+    // different K; index ng and above stand for "no group" (zeros)
+    const uint32_t ng = wave < groups ? (groups - wave + WAVES - 1) / WAVES : 0u;
+    const uint32_t rot = (tile * kRotStride) % groups;
+    auto gphys = [&](uint32_t i) {
+        if (i >= ng)
+            return groups;
+        const uint32_t x = wave + WAVES * i + rot;
+        return x >= groups ? x - groups : x;
     };
 
-    // per-lane operand addresses: row rr of each 16-row block, byte 16 gq of
-    // the step's 64 bytes; the scale byte of that row and 32-element block
-    const uint8_t *wsrc[NBW], *wsc[NBW];
+    // resources over the tile's rows; lane offsets: row rr of each 16-row
+    // block, byte 16 gq of a step's 64 bytes
+    const uint32_t wrows = min((uint32_t)NBW * 16u, g.n - n0);
+    const uint32_t arows = min((uint32_t)MB * 16u, g.m - m0);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(g.w + (size_t)n0 * (g.k / 2u), wrows * (g.k / 2u));
+    const __amdgpu_buffer_rsrc_t wsr = make_rsrc(g.w_scale + (size_t)n0 * kb, wrows * kb);
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.a + (size_t)m0 * g.a_stride, arows * g.a_stride);
+    const __amdgpu_buffer_rsrc_t asr = make_rsrc(g.a_scale + (size_t)m0 * kb, arows * kb);
+    uint32_t wo[NBW], wso[NBW], ao[MB], aso[MB];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-        const uint32_t row = min(n0 + 16u * j + rr, g.n - 1u);
-        wsrc[j] = g.w + (size_t)row * (g.k / 2u) + 16u * gq;
-        wsc[j] = g.w_scale + (size_t)row * kb + gq;
+        wo[j] = (16u * j + rr) * (g.k / 2u) + 16u * gq;
+        wso[j] = (16u * j + rr) * kb;
     }
-    const uint8_t *asrc[MB], *asc[MB];
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-        const uint32_t row = min(m0 + 16u * b + rr, g.m - 1u);
-        asrc[b] = g.a + (size_t)row * g.a_stride + 16u * gq;
-        asc[b] = g.a_scale + (size_t)row * kb + gq;
+        ao[b] = (16u * b + rr) * g.a_stride + 16u * gq;
+        aso[b] = (16u * b + rr) * kb;
     }
 
     f32x4_t acc[NBW][MB];
@@ -149,164 +242,265 @@ __global__ __launch_bounds__(WAVES * 64) void w8a16_w4a4_kernel(MxArgs g)
         for (int b = 0; b < MB; ++b)
             acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t wr[DEPTH][NBW], ar[DEPTH][MB];
-    uint32_t wsr[DEPTH][NBW], asr[DEPTH][MB];
-    auto issue = [&](int d, uint32_t t) {
+    auto issue = [&](MxGroup<MB, NBW> &q, uint32_t gidx) {
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            const u32x4_t *p = reinterpret_cast<const u32x4_t *>(wsrc[j] + t * 64u);
-            wr[d][j] = NTW ? __builtin_nontemporal_load(p) : *p;
-            wsr[d][j] = wsc[j][t * 4u];
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t so = step_off(4u * gidx + e, ksteps);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+                q.w[e][j] = load16<NTW>(wr, wo[j] + so);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                q.a[e][b] = load16<false>(ar, ao[b] + so);
         }
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            ar[d][b] = *reinterpret_cast<const u32x4_t *>(asrc[b] + t * 64u);
-            asr[d][b] = asc[b][t * 4u];
-        }
+        for (int j = 0; j < NBW; ++j)
+            load_scales<SC16>(q.ws[j], wsr, wso[j], gidx, ksteps);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+            load_scales<SC16>(q.as[b], asr, aso[b], gidx, ksteps);
     };
+    // steps past K hold zero data and zero scale bytes (2^-127): they add 0
+    auto compute = [&](const MxGroup<MB, NBW> &q) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if ((uint32_t)d < nw)
-            issue(d, phys(d));
-    for (uint32_t base = 0; base < nw; base += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const uint32_t i = base + d;
-            if (i >= nw)
-                break;
-            u32x4_t cw[NBW], ca[MB];
-            uint32_t cws[NBW], cas[MB];
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                cw[j] = wr[d][j];
-                cws[j] = wsr[d][j];
-            }
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                ca[b] = ar[d][b];
-                cas[b] = asr[d][b];
-            }
-            if (i + DEPTH < nw)
-                issue(d, phys(i + DEPTH));
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
 #pragma unroll
                 for (int b = 0; b < MB; ++b)
-                    acc[j][b] = mx_step(cw[j], cws[j], ca[b], cas[b], acc[j][b]);
+                    acc[j][b] = mx_step(q.w[e][j], scale_byte(q.ws[j][e], gq), q.a[e][b],
+                                        scale_byte(q.as[b][e], gq), acc[j][b]);
+    };
+    // a straight-line ring: every slot issues and computes (a group past
+    // the wave's last reads zeros and adds 0), so no load sits under a
+    // branch; the scheduling barrier keeps each prefetch ahead of the
+    // compute that follows it
+    MxGroup<MB, NBW> buf[kTileBufs];
+#pragma unroll
+    for (int s = 0; s < kTileBufs - 1; ++s)
+        issue(buf[s], gphys(s));
+    for (uint32_t i = 0; i < ng; i += kTileBufs) {
+#pragma unroll
+        for (int s = 0; s < kTileBufs; ++s) {
+            issue(buf[(s + kTileBufs - 1) % kTileBufs], gphys(i + s + kTileBufs - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(buf[s]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     reduce_store<MB, NBW, WAVES>(g, acc, m0, n0, wave, lane);
 }
 
-// Persistent kernel: A (MB 16-row blocks, all of K) and its scales staged in
-// LDS once; each wave pulls 16-row weight tiles from counters[0].
-template <int MB, int WAVES, int DEPTH>
+// Persistent kernel.  Workgroup g owns the contiguous 16-row weight tiles
+// [g n16 / G, (g + 1) n16 / G) and all of their K: items (tile, group of 4
+// K steps), tile-major, split into WAVES equal contiguous ranges, one per
+// wave.  A (MB 16-row blocks, all of K, rows padded by 16 bytes) and its
+// scale bytes are staged in LDS once; each wave then streams its weight
+// items with kPsBufs groups in flight.  A wave that covers a whole
+// tile stores it; a tile split between waves leaves one partial per wave
+// in LDS (slot 0 for the wave's first tile, slot 1 for its last), and the
+// wave holding the tile's first item adds them in wave order.
+template <int MB, int WAVES, bool SC16>
 __global__ __launch_bounds__(WAVES * 64) void w8a16_w4a4_ps_kernel(MxArgs g)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t ksteps = g.k / 128u;
-    const uint32_t kb = g.k / 32u;
-    const uint32_t pitch = g.k / 2u + 16u;            // LDS row pitch of A (bytes)
+    const uint32_t kb = g.k / 32u;                     // scale bytes per row
+    const uint32_t groups = (ksteps + 3u) / 4u;
+    const uint32_t cpr = g.k / 32u;                    // 16-byte chunks per row
+    const uint32_t pitch = 16u * (cpr + 1u);           // LDS row pitch of A (bytes)
+    const uint32_t abytes = w4a4_ps_a_bytes(MB, g.k);
+    const uint32_t sbytes = w4a4_ps_s_bytes(MB, g.k);
     uint8_t *alds = lds;                               // [MB * 16][pitch]
-    uint8_t *slds = lds + MB * 16u * pitch;            // [MB * 16][kb]
+    uint8_t *slds = lds + abytes;                      // [MB * 16][kb]
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(lds + abytes + sbytes);  // [WAVES][2][MB][64]
     const uint32_t rr = lane & 15u, gq = lane >> 4;
 
-    // stage A: 16-byte chunks of each of the MB * 16 rows (rows past m copy
-    // the last valid row), then the scale bytes
-    const uint32_t chunks = g.k / 32u;                 // 16-byte chunks per row
-    for (uint32_t c = threadIdx.x; c < MB * 16u * chunks; c += WAVES * 64u) {
-        const uint32_t r = c / chunks, q = c % chunks;
-        const uint32_t row = min(r, g.m - 1u);
-        *reinterpret_cast<u32x4_t *>(alds + r * pitch + q * 16u) =
-            *reinterpret_cast<const u32x4_t *>(g.a + (size_t)row * g.a_stride + q * 16u);
-    }
-    for (uint32_t c = threadIdx.x; c < MB * 16u * kb; c += WAVES * 64u) {
-        const uint32_t r = c / kb, q = c % kb;
-        slds[c] = g.a_scale[(size_t)min(r, g.m - 1u) * kb + q];
-    }
-    __syncthreads();
+    // tiles and items of this workgroup and wave
+    const uint32_t t_lo = blockIdx.x * g.tiles_base + min(blockIdx.x, g.tiles_extra);
+    const uint32_t items = (g.tiles_base + (blockIdx.x < g.tiles_extra ? 1u : 0u)) * groups;
+    auto range_start = [&](uint32_t w) { return (uint32_t)((uint64_t)w * items / WAVES); };
+    const uint32_t s = range_start(wave), e = range_start(wave + 1u);
 
-    const uint32_t tiles = (g.n + 15u) / 16u;
-    for (;;) {
-        uint32_t t = 0;
-        if (lane == 0)
-            t = __hip_atomic_fetch_add(g.counters, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        t = __builtin_amdgcn_readfirstlane(t);
-        if (t >= tiles)
-            break;
-        const uint32_t n0 = 16u * t;
-        const uint32_t wrow = min(n0 + rr, g.n - 1u);
-        const uint8_t *wsrc = g.w + (size_t)wrow * (g.k / 2u) + 16u * gq;
-        const uint8_t *wsc = g.w_scale + (size_t)wrow * kb + gq;
-        const uint32_t rot = (t * kRotStride) % ksteps;
-        f32x4_t acc[MB];
+    // 1. A and its scales into LDS through registers, in batches of kStageA
+    // 16-byte chunks and kStageS scale dwords per thread.  Thread x copies
+    // row x % R (R = 16 MB rows) of A, chunks x / R + j (threads / R) of
+    // the row; rows past m read zeros.  The last batch's loads are issued
+    // before the weight ring's first groups and written to LDS after them,
+    // so the ring is in flight while A arrives.
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.a, g.m * g.a_stride);
+    const __amdgpu_buffer_rsrc_t asr = make_rsrc(g.a_scale, g.m * kb);
+    constexpr uint32_t kThreads = WAVES * 64u;
+    constexpr uint32_t kRows = MB * 16u;
+    constexpr uint32_t kColStep = kThreads / kRows;    // chunk step of one thread
+    const uint32_t arow = threadIdx.x % kRows, acol = threadIdx.x / kRows;
+    const uint32_t sdwords = sbytes / 4u;
+    const uint32_t a_batches = (cpr + kStageA * kColStep - 1u) / (kStageA * kColStep);
+    const uint32_t s_batches = (sdwords + kStageS * kThreads - 1u) / (kStageS * kThreads);
+    const uint32_t batches = max(a_batches, s_batches);
+    u32x4_t av[kStageA];
+    uint32_t sv[kStageS];
+    auto stage_load = [&](uint32_t bi) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
-            acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        u32x4_t wr[DEPTH];
-        uint32_t wsr[DEPTH];
-        auto phys = [&](uint32_t i) {
-            uint32_t x = i + rot;
-            return x >= ksteps ? x - ksteps : x;
-        };
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d)
-            if ((uint32_t)d < ksteps) {
-                const uint32_t s = phys(d);
-                wr[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(wsrc + s * 64u));
-                wsr[d] = wsc[s * 4u];
-            }
-        for (uint32_t base = 0; base < ksteps; base += DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const uint32_t i = base + d;
-                if (i >= ksteps)
-                    break;
-                const uint32_t s = phys(i);
-                const u32x4_t cw = wr[d];
-                const uint32_t cws = wsr[d];
-                if (i + DEPTH < ksteps) {
-                    const uint32_t s2 = phys(i + DEPTH);
-                    wr[d] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4_t *>(wsrc + s2 * 64u));
-                    wsr[d] = wsc[s2 * 4u];
-                }
-#pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    const uint32_t r = 16u * b + rr;
-                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(alds + r * pitch +
-                                                                       s * 64u + 16u * gq);
-                    const uint32_t as = slds[r * kb + s * 4u + gq];
-                    acc[b] = mx_step(cw, cws, a, as, acc[b]);
-                }
-            }
+        for (uint32_t c = 0; c < kStageA; ++c) {
+            const uint32_t ch = acol + (bi * kStageA + c) * kColStep;
+            av[c] = load16<false>(ar, ch < cpr ? arow * g.a_stride + 16u * ch : kOob);
         }
+#pragma unroll
+        for (uint32_t c = 0; c < kStageS; ++c) {
+            const uint32_t q = (bi * kStageS + c) * kThreads + threadIdx.x;
+            sv[c] = load4(asr, q < sdwords ? 4u * q : kOob);
+        }
+    };
+    auto stage_store = [&](uint32_t bi) {
+#pragma unroll
+        for (uint32_t c = 0; c < kStageA; ++c) {
+            const uint32_t ch = acol + (bi * kStageA + c) * kColStep;
+            if (ch < cpr)
+                *reinterpret_cast<u32x4_t *>(alds + arow * pitch + 16u * ch) = av[c];
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kStageS; ++c) {
+            const uint32_t q = (bi * kStageS + c) * kThreads + threadIdx.x;
+            if (q < sdwords)
+                *reinterpret_cast<uint32_t *>(slds + 4u * q) = sv[c];
+        }
+    };
+    for (uint32_t bi = 0; bi + 1u < batches; ++bi) {
+        stage_load(bi);
+        stage_store(bi);
+    }
+    stage_load(batches - 1u);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the weight ring's first groups (buffer loads into registers)
+    const uint32_t wo = rr * (g.k / 2u) + 16u * gq;   // lane offset inside a tile
+    const uint32_t wso = rr * kb;
+    struct Group {
+        u32x4_t w[4];
+        uint32_t ws[4];
+    };
+    // (tile, group) cursors of the next item to issue and to compute:
+    // items are walked in order, so no division per item
+    uint32_t itl = s / groups, igx = s % groups;
+    uint32_t ctl = itl, cgx = igx;
+    auto issue = [&](Group &q, uint32_t i) {
+        const bool ok = i < e;
+        const uint32_t tl = ok ? itl : 0u;
+        const uint32_t gidx = ok ? igx : groups;
+        if (++igx == groups) {
+            igx = 0;
+            ++itl;
+        }
+        const uint32_t t = t_lo + tl;
+        const uint32_t rows = min(16u, g.n - 16u * t);
+        const __amdgpu_buffer_rsrc_t wr =
+            make_rsrc(g.w + (size_t)(16u * t) * (g.k / 2u), rows * (g.k / 2u));
+        const __amdgpu_buffer_rsrc_t wsr = make_rsrc(g.w_scale + (size_t)(16u * t) * kb, rows * kb);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+            q.w[e4] = load16<true>(wr, wo + step_off(4u * gidx + e4, ksteps));
+        load_scales<SC16>(q.ws, wsr, wso, gidx, ksteps);
+    };
+    Group buf[kPsBufs];
+#pragma unroll
+    for (int b = 0; b < kPsBufs - 1; ++b)
+        issue(buf[b], s + b);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store(batches - 1u);
+    barrier_lds();
+
+    // 3. the wave's items; a tile ends at its last group or the range's end
+    const uint32_t t_first = s / groups;
+    f32x4_t acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto store_tile = [&](const f32x4_t (&v)[MB], uint32_t tl) {
         // lane l holds C[row l % 16 of block b][n0 + 4 (l / 16) .. +3]
+        const uint32_t col = 16u * (t_lo + tl) + 4u * gq;
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
             const uint32_t row = 16u * b + rr;
-            const uint32_t col = n0 + 4u * gq;
             if (row < g.m) {
                 uint16_t *dst = reinterpret_cast<uint16_t *>(g.c) + (size_t)row * g.c_stride + col;
-                const float v[4] = {acc[b].x, acc[b].y, acc[b].z, acc[b].w};
+                const float x[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (col + e < g.n)
-                        dst[e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                for (int e4 = 0; e4 < 4; ++e4)
+                    if (col + e4 < g.n)
+                        dst[e4] = (uint16_t)f32_to_bf16_bits(x[e4]);
             }
         }
+    };
+    auto compute = [&](const Group &q, uint32_t i) {
+        const uint32_t tl = ctl, gidx = cgx;
+        if (++cgx == groups) {
+            cgx = 0;
+            ++ctl;
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const uint32_t t = 4u * gidx + e4;
+            const uint32_t tk = t < ksteps ? t : 0u;   // past K: zero weight, any A
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const uint32_t r = 16u * b + rr;
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(alds + r * pitch +
+                                                                     64u * tk + 16u * gq);
+                const uint32_t as = *reinterpret_cast<const uint32_t *>(slds + r * kb + 4u * tk);
+                acc[b] = mx_step(q.w[e4], scale_byte(q.ws[e4], gq), a, scale_byte(as, gq), acc[b]);
+            }
+        }
+        if (gidx == groups - 1u || i == e - 1u) {
+            if (tl * groups >= s && (tl + 1u) * groups <= e) {
+                store_tile(acc, tl);
+            } else {
+                const uint32_t slot = tl == t_first ? 0u : 1u;
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    part[((wave * 2u + slot) * MB + b) * 64u + lane] = acc[b];
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    for (uint32_t i = s; i < e; i += kPsBufs) {
+#pragma unroll
+        for (int b = 0; b < kPsBufs; ++b) {
+            issue(buf[(b + kPsBufs - 1) % kPsBufs], i + b + kPsBufs - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + b < e)
+                compute(buf[b], i + b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    // The last workgroup to finish puts both counters back to zero: by then
-    // every wave has taken its final ticket.
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(g.counters + 1, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1u) {
-            __hip_atomic_store(g.counters, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(g.counters + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // 4. split tiles: the wave whose range holds a tile's first item but not
+    // its last (that tile is the wave's last) adds its own partial and the
+    // slot-0 partials of the following waves that start inside the tile
+    if (e > s) {
+        const uint32_t tl = (e - 1u) / groups;
+        if (tl * groups >= s && (tl + 1u) * groups > e) {
+            const uint32_t slot = tl == t_first ? 0u : 1u;
+            f32x4_t sum[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                sum[b] = part[((wave * 2u + slot) * MB + b) * 64u + lane];
+            for (uint32_t w = wave + 1u; w < (uint32_t)WAVES; ++w) {
+                const uint32_t ws0 = range_start(w), we0 = range_start(w + 1u);
+                if (ws0 >= (tl + 1u) * groups)
+                    break;
+                if (we0 > ws0) {
+#pragma unroll
+                    for (int b = 0; b < MB; ++b)
+                        sum[b] += part[((w * 2u) * MB + b) * 64u + lane];
+                }
+            }
+            store_tile(sum, tl);
         }
     }
 }
@@ -323,35 +517,56 @@ hipError_t launch_mx(K kern, const MxArgs &g, const w8a16_plan_t &p, hipStream_t
     return hipGetLastError();
 }
 
-template <int MB, int NBW, bool NTW>
-hipError_t launch_w4a4_mnt(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+template <int MB, int NBW, bool NTW, bool SC16>
+hipError_t launch_w4a4_v(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
     static std::atomic<uint64_t> lds_set[3];
     switch (p.waves) {
-    case 4: return launch_mx(w8a16_w4a4_kernel<MB, NBW, 4, 2, NTW>, g, p, stream, lds_set[0]);
-    case 8: return launch_mx(w8a16_w4a4_kernel<MB, NBW, 8, 2, NTW>, g, p, stream, lds_set[1]);
-    case 16: return launch_mx(w8a16_w4a4_kernel<MB, NBW, 16, 2, NTW>, g, p, stream, lds_set[2]);
-    default: return hipErrorInvalidValue;
+    case 4:
+        return launch_mx(w8a16_w4a4_kernel<MB, NBW, 4, NTW, SC16>, g, p, stream, lds_set[0]);
+    case 8:
+        if constexpr (w4a4_variant_ok(MB, NBW, 8))
+            return launch_mx(w8a16_w4a4_kernel<MB, NBW, 8, NTW, SC16>, g, p, stream, lds_set[1]);
+        break;
+    case 16:
+        if constexpr (w4a4_variant_ok(MB, NBW, 16))
+            return launch_mx(w8a16_w4a4_kernel<MB, NBW, 16, NTW, SC16>, g, p, stream, lds_set[2]);
+        break;
+    default: break;
     }
+    return hipErrorInvalidValue;
 }
 
+// Nontemporal weight loads when no other row tile reads the same weight;
+// 16-byte scale loads when every group of 4 K steps is whole.
 template <int MB, int NBW>
 hipError_t launch_w4a4_mn(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
+    const bool sc16 = g.k % 512u == 0;
     if (g.m_tiles == 1)
-        return launch_w4a4_mnt<MB, NBW, true>(g, p, stream);
-    return launch_w4a4_mnt<MB, NBW, false>(g, p, stream);
+        return sc16 ? launch_w4a4_v<MB, NBW, true, true>(g, p, stream)
+                    : launch_w4a4_v<MB, NBW, true, false>(g, p, stream);
+    return sc16 ? launch_w4a4_v<MB, NBW, false, true>(g, p, stream)
+                : launch_w4a4_v<MB, NBW, false, false>(g, p, stream);
+}
+
+template <int MB, bool SC16>
+hipError_t launch_w4a4_ps_v(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream)
+{
+    static std::atomic<uint64_t> lds_set[3];
+    switch (p.waves) {
+    case 4: return launch_mx(w8a16_w4a4_ps_kernel<MB, 4, SC16>, g, p, stream, lds_set[0]);
+    case 8: return launch_mx(w8a16_w4a4_ps_kernel<MB, 8, SC16>, g, p, stream, lds_set[1]);
+    case 16: return launch_mx(w8a16_w4a4_ps_kernel<MB, 16, SC16>, g, p, stream, lds_set[2]);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int MB>
 hipError_t launch_w4a4_ps_m(const MxArgs &g, const w8a16_plan_t &p, hipStream_t stream)
 {
-    static std::atomic<uint64_t> lds_set[2];
-    switch (p.waves) {
-    case 8: return launch_mx(w8a16_w4a4_ps_kernel<MB, 8, 4>, g, p, stream, lds_set[0]);
-    case 16: return launch_mx(w8a16_w4a4_ps_kernel<MB, 16, 4>, g, p, stream, lds_set[1]);
-    default: return hipErrorInvalidValue;
-    }
+    return g.k % 512u == 0 ? launch_w4a4_ps_v<MB, true>(g, p, stream)
+                           : launch_w4a4_ps_v<MB, false>(g, p, stream);
 }
 
 }  // namespace
@@ -362,6 +577,7 @@ hipError_t launch_w4a4(const MxArgs &g, const w8a16_plan_t &p, hipStream_t strea
         switch (p.m_blocks) {
         case 1: return launch_w4a4_ps_m<1>(g, p, stream);
         case 2: return launch_w4a4_ps_m<2>(g, p, stream);
+        case 4: return launch_w4a4_ps_m<4>(g, p, stream);
         default: return hipErrorInvalidValue;
         }
     }

@@ -93,12 +93,13 @@ typedef enum w8a16_kernel {
     W8A16_KERNEL_W8A8 = 4,
     /* W4A4 MX kernel (w8a16_gemm_w4a4 only): a workgroup owns n_blocks
      * 16-column blocks and m_blocks 16-row blocks of C over all of K, its
-     * waves take interleaved 128-wide K steps with one scaled FP4 MFMA per
-     * block and step, each activation fragment feeding the n_blocks weight
-     * blocks.  No K split. */
+     * waves take interleaved groups of four 128-wide K steps with one scaled
+     * FP4 MFMA per block and step, each activation fragment feeding the
+     * n_blocks weight blocks.  No K split. */
     W8A16_KERNEL_W4A4 = 5,
     /* Persistent W4A4 MX kernel: one workgroup per CU stages all of A in
-     * LDS, its waves pull 16-row weight tiles from a counter. */
+     * LDS; each wave then walks its own 16-row weight tiles, dealt out
+     * round-robin. */
     W8A16_KERNEL_W4A4_PS = 6
 } w8a16_kernel;
 
@@ -314,11 +315,12 @@ int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float 
  *
  * Products are exact, sums FP32 (the matrix cores apply the two block scales
  * to each 32-element partial), one round-to-nearest-even to BF16.  Device
- * pointers owned by the caller.  Errors, in order: m == 0; k not a positive
- * multiple of 128; a_row_stride < k or c_row_stride < n; a_row_stride not a
- * multiple of 32 (16-byte rows); n == 0; a null pointer; m above 64
- * (W8A16_ERR_BAD_PLAN).  The persistent plan uses the (device, stream)
- * workspace's counters (see Ownership).  Asynchronous. */
+ * pointers owned by the caller, 16-byte aligned.  Errors, in order: m == 0;
+ * k not a positive multiple of 128; a_row_stride < k or c_row_stride < n;
+ * a_row_stride not a multiple of 32 (16-byte rows); n == 0; k or
+ * a_row_stride above 2^24 elements (W8A16_ERR_BAD_PLAN: the kernels address
+ * a tile's rows through 32-bit buffer ranges); a null pointer; m above 64
+ * (W8A16_ERR_BAD_PLAN).  No workspace.  Asynchronous. */
 int w8a16_gemm_w4a4(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
                     const void *w_fp4, const uint8_t *w_scale, void *c, uint32_t c_row_stride,
                     uint32_t m, uint32_t n, uint32_t k, void *stream);
@@ -329,7 +331,8 @@ int w8a16_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count,
                     w8a16_plan_t *out);
 
 /* w8a16_gemm_w4a4 with an explicit plan (kernel W8A16_KERNEL_W4A4:
- * m_blocks 1, 2 or 4, n_blocks 1, 2 or 4, waves 4, 8 or 16; kernel
+ * m_blocks 1, 2 or 4 and n_blocks 1, 2 or 4, not both 4, with 4 waves, 8
+ * waves up to m_blocks + n_blocks = 4, 16 waves for 1 x 1; kernel
  * W8A16_KERNEL_W4A4_PS: m_blocks 1 or 2 covering m, waves 8 or 16).  For
  * tests and tuning. */
 int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,

@@ -541,37 +541,88 @@ def _w4a4_cost(m, n, mb, nb, cus=256):
 W4A4_TILES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
 
 
+def _w4a4_ps_lds(mb, k, waves):
+    a = mb * 16 * (k // 2 + 16)
+    sc = -(-(mb * 16 * (k // 32)) // 256) * 256
+    return a + sc + waves * 2 * mb * 1024
+
+
 def test_w4a4_plans_cover_and_take_the_cheapest_tile():
     rng = np.random.default_rng(21)
+    kinds = set()
     for _ in range(300):
         m = int(rng.integers(1, 65))
         n = int(rng.integers(1, 40000))
-        k = 128 * int(rng.integers(1, 65))
+        k = 128 * int(rng.integers(1, 129))
         p = w8.plan_w4a4(m, n, k)
+        kinds.add(p.kernel)
+        mb = 1 if m <= 16 else (2 if m <= 32 else 4)
+        n16 = -(-n // 16)
+        fits = [w for w in (8, 4) if _w4a4_ps_lds(mb, k, w) <= 160 * 1024 - 256]
+        grid = min(256, n16)
+        items = -(-n16 // grid) * -(-(k // 128) // 4)
         if p.kernel == w8.KERNEL_W4A4_PS:
-            assert 8 < m <= 32 and -(-n // 16) >= 8 * 256
-            assert p.grid == 256 and p.counter_count == 2 and p.n_blocks == 1
-            assert 16 * p.m_blocks >= m and p.lds_bytes <= 160 * 1024
+            # two or more tiles per CU and A fits in LDS: 8 waves, 4 for few
+            # items or little LDS room
+            assert fits and n16 >= 2 * 256 and p.m_blocks == mb and p.n_blocks == 1
+            want = 8 if 8 in fits and items >= 8 else 4
+            assert p.waves == want and p.grid == grid, (m, n, k)
+            assert p.counter_count == 0 and p.lds_bytes == _w4a4_ps_lds(mb, k, p.waves)
             continue
+        assert not fits or n16 < 2 * 256, (m, n, k)
         assert p.kernel == w8.KERNEL_W4A4 and p.splits == 1
         assert p.m_tiles * 16 * p.m_blocks >= m and p.n_tiles * 16 * p.n_blocks >= n
         assert p.grid == p.m_tiles * p.n_tiles
         best = min(_w4a4_cost(m, n, mb, nb) for mb, nb in W4A4_TILES)
         assert _w4a4_cost(m, n, p.m_blocks, p.n_blocks) == best, (m, n, k)
         assert p.lds_bytes == p.waves * p.m_blocks * p.n_blocks * 1024
+        assert w4a4_variant_ok(p.m_blocks, p.n_blocks, p.waves)
+        bigger = [w for w in (8, 16) if w > p.waves and w4a4_variant_ok(p.m_blocks, p.n_blocks, w)]
+        assert not bigger or -(-k // 512) < 2 * bigger[0], (m, n, k, p.waves)
+    assert kinds == {w8.KERNEL_W4A4, w8.KERNEL_W4A4_PS}
+
+
+def w4a4_variant_ok(mb, nb, waves):
+    """Register rule of the built tiled W4A4 variants: two groups of 4 K
+    steps of mb + nb operand blocks in flight per wave."""
+    return waves == 4 or (waves == 8 and mb + nb <= 4) or (waves == 16 and mb + nb <= 2)
+
+
+def test_w4a4_explicit_plans_take_exactly_the_built_variants():
+    for mb, nb in W4A4_TILES:
+        for waves in (4, 8, 16):
+            m = 16 * mb
+            if w4a4_variant_ok(mb, nb, waves):
+                p = w8.make_plan(m, 4096, 4096, w8.KERNEL_W4A4, mb, nb, 1, waves=waves)
+                assert (p.block, p.lds_bytes) == (64 * waves, waves * mb * nb * 1024)
+            else:
+                with pytest.raises(w8.W8A16Error) as e:
+                    w8.make_plan(m, 4096, 4096, w8.KERNEL_W4A4, mb, nb, 1, waves=waves)
+                assert e.value.status == w8.ERR_BAD_PLAN
 
 
 def test_w4a4_persistent_rule():
-    # 9..32 rows over at least 8 16-row tiles per CU
-    assert w8.plan_w4a4(16, 32768, 4096).kernel == w8.KERNEL_W4A4_PS
-    assert w8.plan_w4a4(32, 32768, 8192).kernel == w8.KERNEL_W4A4_PS
-    assert w8.plan_w4a4(8, 32768, 4096).kernel == w8.KERNEL_W4A4        # m <= 8
-    assert w8.plan_w4a4(33, 32768, 4096).kernel == w8.KERNEL_W4A4       # m > 32
-    assert w8.plan_w4a4(16, 32752, 4096).kernel == w8.KERNEL_W4A4       # 2047 tiles
-    # A must fit in LDS: 32 rows x 16384 K do not
-    assert w8.plan_w4a4(32, 65536, 16384).kernel == w8.KERNEL_W4A4
+    # persistent with two or more 16-row tiles per CU and A in LDS
+    for m, n, k in [(16, 32768, 4096), (16, 12288, 5120), (1, 8192, 4096), (33, 8192, 1024),
+                    (24, 33000, 2048)]:
+        assert w8.plan_w4a4(m, n, k).kernel == w8.KERNEL_W4A4_PS, (m, n, k)
+    # one tile per CU or so: tiled
+    for m, n, k in [(8, 4096, 4096), (32, 6144, 2048), (3, 1000, 512), (16, 8176, 4096)]:
+        assert w8.plan_w4a4(m, n, k).kernel == w8.KERNEL_W4A4, (m, n, k)
+    # A does not fit: 32 rows x 16384 K, 64 rows x 4096 K
+    for m, n, k in [(32, 65536, 16384), (64, 32768, 4096), (16, 65536, 1 << 16)]:
+        assert w8.plan_w4a4(m, n, k).kernel == w8.KERNEL_W4A4, (m, n, k)
     p = w8.plan_w4a4(12, 40000, 2048, cu_count=100)
-    assert p.kernel == w8.KERNEL_W4A4_PS and p.grid == 100
+    assert p.kernel == w8.KERNEL_W4A4_PS and p.grid == 100 and p.waves == 8
+    p = w8.plan_w4a4(16, 32768, 4096)
+    assert (p.waves, p.grid) == (8, 256)
+    assert p.lds_bytes == 16 * 2064 + 16 * 128 + 8 * 2 * 1024
+    # few items per workgroup: 4 waves
+    p = w8.plan_w4a4(16, 8192, 512)
+    assert (p.kernel, p.waves) == (w8.KERNEL_W4A4_PS, 4)
+    # the tiled kernel gives each wave two groups of 4 K steps
+    p = w8.plan_w4a4(8, 4096, 4096)
+    assert (p.m_blocks, p.n_blocks, p.waves) == (1, 1, 4)
 
 
 def test_w4a4_plan_errors():
@@ -583,12 +634,25 @@ def test_w4a4_plan_errors():
         with pytest.raises(w8.W8A16Error) as e:
             w8.plan_w4a4(*args)
         assert e.value.status == status
+    # K and the A pitch stay within the kernels' 32-bit buffer ranges
+    for m, n, k in [(1, 16, (1 << 24) + 128), (16, 4096, 1 << 25)]:
+        with pytest.raises(w8.W8A16Error) as e:
+            w8.plan_w4a4(m, n, k)
+        assert e.value.status == w8.ERR_BAD_PLAN
+    assert w8.plan_w4a4(1, 16, 1 << 24).kernel == w8.KERNEL_W4A4
     # explicit plans: unsupported tile, waves, persistent rows not covered
     for kern, mb, nb, waves, m in [(w8.KERNEL_W4A4, 4, 4, 8, 64), (w8.KERNEL_W4A4, 1, 8, 8, 16),
                                    (w8.KERNEL_W4A4, 1, 1, 6, 16),
                                    (w8.KERNEL_W4A4_PS, 1, 1, 16, 17),
-                                   (w8.KERNEL_W4A4_PS, 2, 1, 4, 32)]:
+                                   (w8.KERNEL_W4A4_PS, 3, 1, 8, 40),
+                                   (w8.KERNEL_W4A4_PS, 2, 1, 6, 32)]:
         with pytest.raises(w8.W8A16Error):
             w8.make_plan(m, 4096, 4096, kern, mb, nb, 1, waves=waves)
     p = w8.make_plan(17, 4096, 4096, w8.KERNEL_W4A4_PS, 2, 1, 1, waves=8, cu_count=4)
-    assert (p.grid, p.block, p.counter_count) == (4, 512, 2)
+    assert (p.grid, p.block, p.counter_count) == (4, 512, 0)
+    # fewer workgroups than CUs when the weight has fewer 16-row tiles
+    p = w8.make_plan(17, 100 * 16, 4096, w8.KERNEL_W4A4_PS, 2, 1, 1, waves=16)
+    assert p.grid == 100
+    # A and the partial tiles must fit in LDS: 64 rows x 4096 K at 16 waves do not
+    with pytest.raises(w8.W8A16Error):
+        w8.make_plan(64, 4096, 4096, w8.KERNEL_W4A4_PS, 4, 1, 1, waves=16)

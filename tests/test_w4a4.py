@@ -74,14 +74,18 @@ def exact_mx(m, n, k, seed, a_row_stride=None, c_row_stride=None, c_extra_rows=1
 
 
 W4A4_SHAPES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
+# the built variants: two groups of 4 K steps of mb + nb blocks per wave
+W4A4_VARIANTS = [(mb, nb, w) for mb, nb in W4A4_SHAPES for w in (4, 8, 16)
+                 if w == 4 or (w == 8 and mb + nb <= 4) or (w == 16 and mb + nb <= 2)]
 
 
-@pytest.mark.parametrize("mb,nb", W4A4_SHAPES)
-@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("mb,nb,waves", W4A4_VARIANTS)
 def test_exact_data_every_w4a4_variant(w8, mb, nb, waves):
-    """Ragged rows and columns, A pitch padding, K steps not a multiple of
-    the waves, two and more row tiles."""
-    for m, n, k in [(16 * mb - 3, 16 * nb * 3 + 5, 128 * 11), (16 * mb + 1, 16 * nb + 1, 256)]:
+    """Ragged rows and columns, A pitch padding, K steps that leave a
+    partial group of 4 and fewer groups than waves, whole groups of 4
+    (16-byte scale loads), two and more row tiles."""
+    for m, n, k in [(16 * mb - 3, 16 * nb * 3 + 5, 128 * 11), (16 * mb + 1, 16 * nb + 1, 256),
+                    (16 * mb, 16 * nb * 2 - 1, 128 * 12)]:
         if m > 64 or m < 1:
             continue
         p = exact_mx(m, n, k, seed=100 * mb + 10 * nb + waves + m, a_row_stride=k + 64,
@@ -90,20 +94,29 @@ def test_exact_data_every_w4a4_variant(w8, mb, nb, waves):
         check_mx(p, run_mx(w8, p, plan), exact=True)
 
 
-@pytest.mark.parametrize("m", [9, 16, 17, 32])
-@pytest.mark.parametrize("waves", [8, 16])
+# 16 waves' partial tiles of four row blocks alone take 128 KiB of LDS
+PS_CASES = [(m, w) for m in (1, 9, 16, 17, 32, 33, 48) for w in (4, 8, 16) if m <= 32 or w < 16]
+
+
+@pytest.mark.parametrize("m,waves", PS_CASES)
 def test_exact_data_persistent_w4a4(w8, m, waves):
-    """Persistent kernel with 4 workgroups, so each wave pulls many 16-row
-    tiles; two problems back to back on one stream (the tile counter must
-    be back at zero for the second)."""
-    mb = 1 if m <= 16 else 2
-    n, k = 16 * 97 + 7, 128 * 9
+    """Persistent kernel: equal contiguous tile ranges per workgroup, K
+    split over the waves.  Many tiles per wave with whole tiles stored by
+    one wave (4 workgroups), tiles split across several waves (one
+    workgroup, long K), fewer tiles than workgroups, K with a partial group
+    of 4 steps and K of whole groups; calls back to back on one stream."""
+    mb = 1 if m <= 16 else (2 if m <= 32 else 4)
     stream = torch.cuda.Stream()
-    for seed in (1, 2):
-        p = exact_mx(m, n, k, seed=500 + m + waves + seed, a_row_stride=k + 32,
+    cases = [(16 * 97 + 7, 128 * 9, 4), (16 * 97 + 7, 128 * 16, 4), (40, 128 * 15, 1),
+             (16 * 3, 128 * 8, 16)]
+    for seed, (n, k, cus) in enumerate(cases):
+        lds = mb * 16 * (k // 2 + 16) + -(-(mb * 16 * (k // 32)) // 256) * 256 + waves * 2 * mb * 1024
+        if lds > 160 * 1024 - 256:
+            continue                       # A and the waves' partial tiles exceed LDS
+        p = exact_mx(m, n, k, seed=500 + 7 * m + waves + seed, a_row_stride=k + 32,
                      c_row_stride=n + 1)
-        plan = w8.make_plan(m, n, k, w8.KERNEL_W4A4_PS, mb, 1, 1, waves=waves, cu_count=4)
-        assert plan.grid == 4 and plan.counter_count == 2
+        plan = w8.make_plan(m, n, k, w8.KERNEL_W4A4_PS, mb, 1, 1, waves=waves, cu_count=cus)
+        assert plan.grid == min(cus, -(-n // 16)) and plan.counter_count == 0
         check_mx(p, run_mx(w8, p, plan, stream), exact=True)
 
 
@@ -133,7 +146,8 @@ def test_every_e2m1_code_and_scale_lane(w8):
 @pytest.mark.parametrize("m,n,k,pitch", [(8, 4096, 4096, 4096), (16, 12288, 5120, 5120),
                                          (32, 6144, 2048, 2560), (3, 1000, 512, 640),
                                          (64, 2048, 4096, 4096), (16, 32768, 4096, 4096),
-                                         (24, 33000, 2048, 2048)])
+                                         (24, 33000, 2048, 2048), (40, 3000, 1152, 1152),
+                                         (32, 2048, 16384, 16384), (1, 16, 128, 128)])
 def test_w4a4_default_plans_full_parity(w8, m, n, k, pitch):
     """MXFP4-quantized N(0,1) activations and N(0,0.02) weights, default
     plans (tiled and persistent), every output against the oracle."""
@@ -197,6 +211,7 @@ def test_w4a4_argument_errors_leave_c_untouched(w8):
     for i in range(5):
         assert call(k, n, m, n, k, nullify=i) == w8.ERR_NULL_PTR
     assert call(k, n, 65, n, k) == w8.ERR_BAD_PLAN
+    assert call((1 << 24) + 32, n, m, n, k) == w8.ERR_BAD_PLAN     # A pitch past 2^24
     torch.cuda.synchronize()
     assert bool((c == 0x1234).all())
 
