@@ -45,6 +45,35 @@ __device__ __forceinline__ void dequant16(u32x4_t raw, bf16x8_t &lo, bf16x8_t &h
     hi = __builtin_bit_cast(bf16x8_t, h);
 }
 
+// Buffer resources.  A raw buffer load through a resource that spans
+// exactly the bytes it may read returns zeros, without a memory access, for
+// an offset at or past the resource's byte count.  Kernels use that for
+// rows past m or n, K steps past the end and ring prefetches past a wave's
+// last step: the loads need no branches, and the compiler's wait counts
+// stay exact (a load under a branch makes it wait for every load in flight
+// at the next use of any of them).
+constexpr int kRsrcWord3 = 0x00020000;     // raw 32-bit data format, no swizzle
+constexpr uint32_t kOob = 0x80000000u;     // past every resource (each < 2^31 bytes)
+constexpr int kCacheNt = 2;                // nontemporal hint of a load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? kCacheNt : 0));
+}
+
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 // Step offset between the K walks of consecutive tiles (odd, so tile t
 // starts at step 37t mod span and neighbouring tiles are far apart).
 constexpr uint32_t kRotStride = 37;

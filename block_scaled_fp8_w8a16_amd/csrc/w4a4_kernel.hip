@@ -108,34 +108,10 @@ __device__ __forceinline__ void reduce_store(const MxArgs &g, f32x4_t (&acc)[NBW
     }
 }
 
-// Buffer resources.  Every global load of these kernels is a raw buffer
-// load through a resource that spans exactly the rows it may read: an
-// offset at or past the resource's byte count returns zeros without a
-// memory access.  Steps past K, rows past m or n and the prefetch past a
-// wave's last group are such offsets, so the loads need no branches and the
-// compiler's wait counts stay exact (a load under a branch makes it wait for
-// every load in flight).
-constexpr int kRsrcWord3 = 0x00020000;     // raw 32-bit data format, no swizzle
-constexpr uint32_t kOob = 0x80000000u;     // past every resource (each < 2^31 bytes)
-constexpr int kCacheNt = 2;                // nontemporal hint of a load
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
-
-template <bool NT>
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(u32x4_t,
-                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? kCacheNt : 0));
-}
-
-__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
+// Every global load of these kernels is a raw buffer load (make_rsrc,
+// load16, load4): steps past K, rows past m or n and the prefetch past a
+// wave's last group are offsets past the resource, which read zeros, so no
+// load sits under a branch and the compiler's wait counts stay exact.
 
 // Scale dwords of the 4 K steps of group `gidx` for one row (`row_off` =
 // the row's first scale byte in the resource): dword e holds the 4 block

@@ -97,9 +97,10 @@ typedef enum w8a16_kernel {
      * FP4 MFMA per block and step, each activation fragment feeding the
      * n_blocks weight blocks.  No K split. */
     W8A16_KERNEL_W4A4 = 5,
-    /* Persistent W4A4 MX kernel: one workgroup per CU stages all of A in
-     * LDS; each wave then walks its own 16-row weight tiles, dealt out
-     * round-robin. */
+    /* Persistent W4A4 MX kernel: one workgroup per CU owns an equal
+     * contiguous range of 16-row weight tiles and stages all of A in LDS;
+     * its waves split the range's (tile, 4-step K group) items evenly and
+     * add the partials of tiles split between them in wave order. */
     W8A16_KERNEL_W4A4_PS = 6
 } w8a16_kernel;
 
