@@ -13,7 +13,7 @@ import pytest
 
 import datagen
 import oracle
-from variants import tile_variants
+from variants import plan_ok, tile_variants
 
 pytestmark = pytest.mark.gpu
 
@@ -148,20 +148,28 @@ STREAM_SHAPES = [(1, 1), (1, 2), (1, 3), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4),
                  (4, 1), (4, 2)]
 
 
-@pytest.mark.parametrize("mb,nb", STREAM_SHAPES)
-@pytest.mark.parametrize("depth", [1, 2, 4])
-@pytest.mark.parametrize("direct", [0, 1])
-@pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("waves", [4, 8, 16])
+# The collection-time filters below pass the plan's kernel and flag codes as
+# numbers (kernel 1 stream, 2 tile, 3 ring; flag 4 XCD-local grouping): the
+# package is imported inside plan_ok only.
+def _stream_case(mb, nb, splits):
+    return 16 * mb - 3, 16 * nb * 3 + 5, 1024 if splits == 1 else 128 * 7
+
+
+# every (shape, depth, A staging, splits, waves) the stream kernel's planner
+# accepts (the rest need more LDS than a CU has)
+STREAM_VARIANTS = [(mb, nb, depth, direct, splits, waves)
+                   for mb, nb in STREAM_SHAPES for depth in (1, 2, 4) for direct in (0, 1)
+                   for splits in (1, 3) for waves in (4, 8, 16)
+                   if plan_ok(*_stream_case(mb, nb, splits), 1, mb, nb, splits, depth=depth,
+                              flags=direct, waves=waves)]
+
+
+@pytest.mark.parametrize("mb,nb,depth,direct,splits,waves", STREAM_VARIANTS)
 def test_exact_data_every_stream_variant(w8, mb, nb, depth, direct, splits, waves):
-    m, n, k = 16 * mb - 3, 16 * nb * 3 + 5, 1024 if splits == 1 else 128 * 7
+    m, n, k = _stream_case(mb, nb, splits)
     p = exact_problem(m, n, k, seed=100 * mb + 10 * nb + splits + 1000 * depth + waves)
-    try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=depth,
-                            flags=direct, waves=waves)
-    except w8.W8A16Error as e:
-        assert e.status == w8.ERR_BAD_PLAN and "LDS" in str(e)
-        pytest.skip("variant needs more LDS than a CU has")
+    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=depth,
+                        flags=direct, waves=waves)
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
 
@@ -187,23 +195,28 @@ def run_gpu_pair(w8, p1, p2, plan, stream):
 XCD_SHAPES = STREAM_SHAPES + [(2, 8)]
 
 
-@pytest.mark.parametrize("mb,nb", XCD_SHAPES)
-@pytest.mark.parametrize("splits,ksteps", [(2, 16), (4, 13), (8, 64)])
-@pytest.mark.parametrize("waves", [4, 8, 16])
+def _xcd_case(mb, nb, ksteps):
+    return 16 * mb - 3, 16 * nb * 8 - 5, 128 * ksteps
+
+
+XCD_VARIANTS = [(mb, nb, splits, ksteps, waves)
+                for mb, nb in XCD_SHAPES for splits, ksteps in ((2, 16), (4, 13), (8, 64))
+                for waves in (4, 8, 16)
+                if plan_ok(*_xcd_case(mb, nb, ksteps), 1, mb, nb, splits, depth=1, flags=4,
+                           waves=waves)]
+
+
+@pytest.mark.parametrize("mb,nb,splits,ksteps,waves", XCD_VARIANTS)
 def test_exact_data_xcd_local_splits(w8, mb, nb, splits, ksteps, waves):
     """Split plans grouped per XCD: 8 tiles (one per XCD range), two
     different problems back to back on one stream, so a partial read
     before its writer's stores completed (or a stale one from the previous
     call) breaks bit exactness."""
-    m, n, k = 16 * mb - 3, 16 * nb * 8 - 5, 128 * ksteps
+    m, n, k = _xcd_case(mb, nb, ksteps)
     p1 = exact_problem(m, n, k, seed=7000 + 100 * mb + 10 * nb + splits + waves)
     p2 = exact_problem(m, n, k, seed=9000 + 100 * mb + 10 * nb + splits + waves)
-    try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1,
-                            flags=w8.FLAG_XCD_LOCAL, waves=waves)
-    except w8.W8A16Error as e:
-        assert e.status == w8.ERR_BAD_PLAN and "LDS" in str(e)
-        pytest.skip("variant needs more LDS than a CU has")
+    plan = w8.make_plan(m, n, k, w8.KERNEL_STREAM, mb, nb, splits, depth=1,
+                        flags=w8.FLAG_XCD_LOCAL, waves=waves)
     assert plan.grid == 8 * plan.splits and plan.flags == w8.FLAG_XCD_LOCAL
     g1, g2 = run_gpu_pair(w8, p1, p2, plan, torch.cuda.Stream())
     check_full(p1, g1, exact=True)
@@ -273,23 +286,26 @@ def test_default_split_plans_at_size_sampled(w8, m, n, k):
 RING_SHAPES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)]
 
 
-@pytest.mark.parametrize("mb,nb", RING_SHAPES)
-@pytest.mark.parametrize("sk", [4, 8])
-@pytest.mark.parametrize("depth", [2, 3, 4])
-@pytest.mark.parametrize("wv", [8, 16])
-@pytest.mark.parametrize("msmall", [False, True])
+def _ring_case(mb, nb, sk, depth, msmall):
+    return 5 if msmall else 16 * mb - 3, 16 * nb * 3 + 5, 128 * (sk * (depth + 1) + 3)
+
+
+# the 8-row A staging (msmall) applies to one M block; ring variants that
+# are not built are not collected
+RING_VARIANTS = [(mb, nb, sk, depth, wv, msmall)
+                 for mb, nb in RING_SHAPES for sk in (4, 8) for depth in (2, 3, 4)
+                 for wv in (8, 16) for msmall in (False, True)
+                 if (not msmall or mb == 1) and
+                 plan_ok(*_ring_case(mb, nb, sk, depth, msmall), 3, mb, nb, 1, depth=depth,
+                         flags=0, waves=wv, stage_steps=sk)]
+
+
+@pytest.mark.parametrize("mb,nb,sk,depth,wv,msmall", RING_VARIANTS)
 def test_exact_data_every_ring_variant(w8, mb, nb, sk, depth, wv, msmall):
     """More stages than ring slots, a ragged last stage, ragged m and n."""
-    if msmall and mb != 1:
-        pytest.skip("the 8-row A staging applies to one M block")
-    m = 5 if msmall else 16 * mb - 3
-    n, k = 16 * nb * 3 + 5, 128 * (sk * (depth + 1) + 3)
-    try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_RING, mb, nb, 1, depth=depth, flags=0,
-                            waves=wv, stage_steps=sk)
-    except w8.W8A16Error as e:
-        assert e.status == w8.ERR_BAD_PLAN
-        pytest.skip("no such ring variant: %s" % e)
+    m, n, k = _ring_case(mb, nb, sk, depth, msmall)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_RING, mb, nb, 1, depth=depth, flags=0,
+                        waves=wv, stage_steps=sk)
     assert plan.flags == (w8.FLAG_A8 if msmall else 0)
     p = exact_problem(m, n, k, seed=mb * 1000 + nb * 100 + sk * 10 + depth + wv)
     check_full(p, run_gpu(w8, p, plan), exact=True)
@@ -320,29 +336,31 @@ def test_ring_kernel_strides_and_short_k(w8):
 TILE_VARIANTS = tile_variants()
 
 
-@pytest.mark.parametrize("mb,nb,depth,a_depth", TILE_VARIANTS)
-@pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("m", [40, 128, 200])
-@pytest.mark.parametrize("waves", [4, 6, 8, 10])
+# producer-wave layouts (6 and 10 waves) that are not built for a ring
+# size are not collected
+TILE_CASES = [(mb, nb, depth, a_depth, splits, m, waves)
+              for mb, nb, depth, a_depth in TILE_VARIANTS for splits in (1, 3)
+              for m in (40, 128, 200) for waves in (4, 6, 8, 10)
+              if plan_ok(m, 16 * nb * 3 + 7, 128 * 23, 2, mb, nb, splits, depth=depth,
+                         a_depth=a_depth, waves=waves)]
+
+
+@pytest.mark.parametrize("mb,nb,depth,a_depth,splits,m,waves", TILE_CASES)
 def test_exact_data_every_tile_variant(w8, mb, nb, depth, a_depth, splits, m, waves):
     """K long enough for both rings to wrap, in every split; 8 waves split
     every K step between two groups; 6 and 10 add two producer waves."""
     n, k = 16 * nb * 3 + 7, 128 * 23
     p = exact_problem(m, n, k, seed=7 * m + nb + 10 * depth + 100 * splits + a_depth + waves + mb)
-    try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, mb, nb, splits, depth=depth,
-                            a_depth=a_depth, waves=waves)
-    except w8.W8A16Error as e:
-        assert e.status == w8.ERR_BAD_PLAN and "wave variant" in str(e)
-        pytest.skip("variant not built: %s" % e)
+    plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, mb, nb, splits, depth=depth,
+                        a_depth=a_depth, waves=waves)
     assert plan.block == 64 * waves
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
 
 
-@pytest.mark.parametrize("m", [1, 65, 128, 200])
-@pytest.mark.parametrize("splits", [1, 2, 3])
-@pytest.mark.parametrize("n,ksteps", [(507, 8), (300, 7), (256, 1), (1031, 5)])
+@pytest.mark.parametrize("m,splits,n,ksteps",
+                         [(m, sp, n, ks) for m in (1, 65, 128, 200) for sp in (1, 2, 3)
+                          for n, ks in ((507, 8), (300, 7), (256, 1), (1031, 5)) if sp <= ks])
 def test_exact_data_wide_tile(w8, m, splits, n, ksteps):
     """128 x 256 tiles (32x32x16 MFMAs, weight ring of 3 steps, A ring of 3
     half steps): ragged rows and columns, one and several row tiles, K
@@ -350,11 +368,7 @@ def test_exact_data_wide_tile(w8, m, splits, n, ksteps):
     k = 128 * ksteps
     p = exact_problem(m, n, k, seed=31 * m + n + 7 * splits + ksteps, a_row_stride=k + 40,
                       c_row_stride=n + 9, c_extra_rows=2)
-    try:
-        plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, 16, splits, depth=3, a_depth=3)
-    except w8.W8A16Error as e:
-        assert e.status == w8.ERR_BAD_PLAN and splits > ksteps
-        pytest.skip("more splits than K steps")
+    plan = w8.make_plan(m, n, k, w8.KERNEL_TILE, 8, 16, splits, depth=3, a_depth=3)
     assert plan.block == 256 and plan.lds_bytes == 147968
     g = run_gpu(w8, p, plan)
     check_full(p, g, exact=True)
