@@ -41,6 +41,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) + µs/call, W8A16 GEMM at M=1..32"
+METRIC_W8A8 = "achieved HBM GB/s (% of peak) + µs/call, W8A8 GEMM (FP8 activations) at M=8..32"
+METRIC_W4A4 = "achieved HBM GB/s (% of peak) + µs/call, W4A4 MXFP4 GEMV at M=8..32"
 MAIN_WORKLOAD = "m8_n4096_k4096"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense BF16 MFMA
@@ -721,7 +723,7 @@ def w4a4_bench(steps: int = 100, warmup: int = 10):
         plan = w8.plan_w4a4(m, n, k, cus)
         kname = "w8a16_w4a4_ps_kernel" if plan.kernel == w8.KERNEL_W4A4_PS else "w8a16_w4a4_kernel"
         print(json.dumps({
-            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "metric": METRIC_W4A4, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
             "config": {"workload": "w4a4_m%d_n%d_k%d" % (m, n, k), "m": m, "n": n, "k": k,
@@ -818,7 +820,7 @@ def w8a8_bench(steps: int = 100, warmup: int = 10):
         gbs = g_bytes / (ms_g * 1e-3) / 1e9
         plan = w8.plan_w8a8(m, n, k, cus)
         print(json.dumps({
-            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "metric": METRIC_W8A8, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": ms_g, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
             "config": {"workload": "w8a8_" + name, "m": m, "n": n, "k": k, "weights": "cold",
