@@ -31,6 +31,7 @@ ERR_NULL_PTR = 6
 ERR_BAD_PLAN = 7
 ERR_HIP = 8
 ERR_WORKSPACE = 9
+ERR_ENV = 10
 
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
@@ -420,10 +421,16 @@ def gemm_w8a8(qa, a_scales, w, scale, c=None, *, plan_: Optional[Plan] = None, s
     for t in (a_scales, scale):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("scales must be contiguous float32")
+    ks = k // 128 if k % 128 == 0 else 0
+    if a_scales.numel() < m * ks or scale.numel() < (n + 127) // 128 * ks:
+        raise ValueError("a_scales must hold [m, k/128] and scale [ceil(n/128), k/128] values")
     if c is None:
         c = torch.empty((m, n), dtype=torch.bfloat16, device=qa.device)
     if c.dtype != torch.bfloat16 or c.stride(1) != 1 or tuple(c.shape) != (m, n):
         raise ValueError("c must be bfloat16 [m, n] with unit column stride")
+    for t in (qa, a_scales, w, scale, c):
+        if not t.is_cuda:
+            raise ValueError("all operands must be GPU tensors")
     if stream is None:
         stream = torch.cuda.current_stream(qa.device)
     q_rs = qa.stride(0) if m > 1 else max(qa.stride(0), k)

@@ -8,9 +8,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <set>
+#include <string>
 #include <utility>
 #include <vector>
 
@@ -46,6 +49,119 @@ int hip_fail(hipError_t e, const char *what)
     char buf[256];
     snprintf(buf, sizeof buf, "w8a16_gemm: %s failed: %s", what, hipGetErrorString(e));
     return fail(W8A16_ERR_HIP, buf);
+}
+
+// ---- diagnostics ---------------------------------------------------------
+// W8A16_LOG (print each distinct launch and its plan once) and
+// W8A16_DEBUG_SYNC (wait for the stream after each launch and report a
+// failed kernel), read once per process.  Unset, empty or "0" is off, "1"
+// is on; any other value fails every enqueuing call with W8A16_ERR_ENV.
+struct Levers {
+    int status = W8A16_OK;
+    bool log = false;
+    bool debug_sync = false;
+    char msg[160] = "";
+};
+
+Levers read_levers()
+{
+    Levers l;
+    const char *names[2] = {"W8A16_LOG", "W8A16_DEBUG_SYNC"};
+    bool *flags[2] = {&l.log, &l.debug_sync};
+    for (int i = 0; i < 2; ++i) {
+        const char *v = std::getenv(names[i]);
+        if (!v || !*v || std::strcmp(v, "0") == 0)
+            continue;
+        if (std::strcmp(v, "1") == 0) {
+            *flags[i] = true;
+            continue;
+        }
+        l.status = W8A16_ERR_ENV;
+        snprintf(l.msg, sizeof l.msg, "%s='%.48s' must be 0 or 1", names[i], v);
+        break;
+    }
+    return l;
+}
+
+const Levers &levers()
+{
+    static const Levers l = read_levers();
+    return l;
+}
+
+int check_levers(const char *entry)
+{
+    const Levers &l = levers();
+    if (l.status == W8A16_OK)
+        return W8A16_OK;
+    char buf[224];
+    snprintf(buf, sizeof buf, "%s: %s", entry, l.msg);
+    return fail(l.status, buf);
+}
+
+const char *kernel_name(uint32_t kernel)
+{
+    switch (kernel) {
+    case W8A16_KERNEL_STREAM: return "stream";
+    case W8A16_KERNEL_TILE: return "tile";
+    case W8A16_KERNEL_RING: return "ring";
+    case W8A16_KERNEL_W8A8: return "w8a8";
+    case W8A16_KERNEL_W4A4: return "w4a4";
+    case W8A16_KERNEL_W4A4_PS: return "w4a4-persistent";
+    default: return "?";
+    }
+}
+
+std::mutex g_log_mutex;
+std::set<std::string> g_logged;   // lines already printed (at most 4096 kept)
+
+void log_line(const char *line)
+{
+    std::lock_guard<std::mutex> lock(g_log_mutex);
+    if (g_logged.size() >= 4096 || !g_logged.insert(line).second)
+        return;
+    std::fputs(line, stderr);
+}
+
+// Under W8A16_LOG=1: the launch of `entry` with plan `p`; `why` is the
+// planner's reason, or null for a caller's plan.
+void log_plan(const char *entry, uint32_t m, uint32_t n, uint32_t k, const w8a16_plan_t &p,
+              const char *why)
+{
+    if (!levers().log)
+        return;
+    char line[640];
+    snprintf(line, sizeof line,
+             "w8a16: %s m=%u n=%u k=%u: kernel=%s tile=%ux%u splits=%u (%u K steps each) "
+             "waves=%u depth=%u stage_steps=%u a_depth=%u flags=0x%x grid=%u block=%u "
+             "lds=%u workspace=%llu: %s\n",
+             entry, m, n, k, kernel_name(p.kernel), 16 * p.m_blocks, 16 * p.n_blocks,
+             p.splits, p.steps_per_split, p.waves, p.depth, p.stage_steps, p.a_depth, p.flags,
+             p.grid, p.block, p.lds_bytes, (unsigned long long)p.workspace_bytes,
+             why ? why : "caller's plan");
+    log_line(line);
+}
+
+// Success epilogue of a call that enqueued work: clears the last error and,
+// under W8A16_DEBUG_SYNC=1, waits for the stream (unless it is being
+// captured, when nothing has run yet) and reports a failed kernel.
+int launched(hipStream_t stream)
+{
+    if (levers().debug_sync) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamIsCapturing");
+        if (cs == hipStreamCaptureStatusNone) {
+            e = hipStreamSynchronize(stream);
+            if (e == hipSuccess)
+                e = hipGetLastError();
+            if (e != hipSuccess)
+                return hip_fail(e, "kernel (checked under W8A16_DEBUG_SYNC)");
+        }
+    }
+    set_last_error("");
+    return W8A16_OK;
 }
 
 int device_cu_count(int dev, uint32_t *out)
@@ -186,9 +302,10 @@ int check_call(const void *a, uint32_t a_row_stride, const void *w_fp8,
 
 // Enqueue the plan's kernels.  `fixed`: the split-K workspace to use (the
 // no-alloc entry's scratch); null takes the (device, stream) workspace.
-int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *block_scale,
-        void *c, uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,
-        const w8a16_plan_t &plan, hipStream_t stream, const Workspace *fixed = nullptr)
+int run(const char *entry, const char *why, const void *a, uint32_t a_row_stride,
+        const void *w_fp8, const float *block_scale, void *c, uint32_t c_row_stride,
+        uint32_t m, uint32_t n, uint32_t k, const w8a16_plan_t &plan, hipStream_t stream,
+        const Workspace *fixed = nullptr)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -232,8 +349,8 @@ int run(const void *a, uint32_t a_row_stride, const void *w_fp8, const float *bl
                                : launch_tile_m128(g, plan, stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
-    set_last_error("");
-    return W8A16_OK;
+    log_plan(entry, m, n, k, plan, why);
+    return launched(stream);
 }
 
 }  // namespace
@@ -247,7 +364,10 @@ int w8a16_gemm(const void *a, uint32_t a_row_stride, const void *w_fp8,
                uint32_t n, uint32_t k, void *stream)
 {
     using namespace w8a16;
-    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    int st = check_levers("w8a16_gemm");
+    if (st != W8A16_OK)
+        return st;
+    st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
     if (st != W8A16_OK)
         return st;
     int dev = 0;
@@ -262,8 +382,8 @@ int w8a16_gemm(const void *a, uint32_t a_row_stride, const void *w_fp8,
     st = make_plan(m, n, k, cus, &plan);
     if (st != W8A16_OK)
         return st;
-    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan,
-               static_cast<hipStream_t>(stream));
+    return run("w8a16_gemm", plan_reason(), a, a_row_stride, w_fp8, block_scale, c,
+               c_row_stride, m, n, k, plan, static_cast<hipStream_t>(stream));
 }
 
 int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
@@ -272,7 +392,10 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
                        void *stream)
 {
     using namespace w8a16;
-    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    int st = check_levers("w8a16_gemm_planned");
+    if (st != W8A16_OK)
+        return st;
+    st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
     if (st != W8A16_OK)
         return st;
     if (!plan)
@@ -284,8 +407,8 @@ int w8a16_gemm_planned(const void *a, uint32_t a_row_stride, const void *w_fp8,
     if (p.kernel == W8A16_KERNEL_W8A8)
         return fail(W8A16_ERR_BAD_PLAN, "w8a16_gemm_planned: the W8A8 kernel takes FP8 "
                                         "activations (w8a16_gemm_w8a8_planned)");
-    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, p,
-               static_cast<hipStream_t>(stream));
+    return run("w8a16_gemm_planned", nullptr, a, a_row_stride, w_fp8, block_scale, c,
+               c_row_stride, m, n, k, p, static_cast<hipStream_t>(stream));
 }
 
 int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride, const void *w_fp8,
@@ -293,7 +416,10 @@ int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride, const void *w_fp8,
                        uint32_t n, uint32_t k, void *stream)
 {
     using namespace w8a16;
-    int st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    int st = check_levers("w8a16_gemm_noalloc");
+    if (st != W8A16_OK)
+        return st;
+    st = check_call(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
     if (st != W8A16_OK)
         return fail_with_name(st, "w8a16_gemm_noalloc");
     int dev = 0;
@@ -310,7 +436,8 @@ int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride, const void *w_fp8,
         return st;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (plan.splits == 1)
-        return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan, hs);
+        return run("w8a16_gemm_noalloc", plan_reason(), a, a_row_stride, w_fp8, block_scale,
+                   c, c_row_stride, m, n, k, plan, hs);
     if (plan.workspace_bytes > kScratchPartialBytes || plan.counter_count > kScratchCounterWords) {
         char buf[256];
         snprintf(buf, sizeof buf,
@@ -330,16 +457,20 @@ int w8a16_gemm_noalloc(const void *a, uint32_t a_row_stride, const void *w_fp8,
     wsp.ws_bytes = kScratchPartialBytes;
     wsp.counters = reinterpret_cast<uint32_t *>(ptr + kScratchPartialBytes);
     wsp.counter_count = (uint32_t)kScratchCounterWords;
-    return run(a, a_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k, plan, hs, &wsp);
+    return run("w8a16_gemm_noalloc", plan_reason(), a, a_row_stride, w_fp8, block_scale, c,
+               c_row_stride, m, n, k, plan, hs, &wsp);
 }
 
 int w8a16_act_quant_fp8(const void *a, uint32_t a_row_stride, void *q, uint32_t q_row_stride,
                         float *scales, uint32_t m, uint32_t k, void *stream)
 {
     using namespace w8a16;
+    int st = check_levers("w8a16_act_quant_fp8");
+    if (st != W8A16_OK)
+        return st;
     // m, k, the A pitch and its alignment as w8a16_gemm checks them (n = 1
     // stands for the absent output width), then the code pitch.
-    int st = check_args(m, 1, k, a_row_stride, 1);
+    st = check_args(m, 1, k, a_row_stride, 1);
     if (st != W8A16_OK)
         return fail_with_name(st, "w8a16_act_quant_fp8");
     char buf[192];
@@ -367,8 +498,13 @@ int w8a16_act_quant_fp8(const void *a, uint32_t a_row_stride, void *q, uint32_t 
     hipError_t e = launch_act_quant(qa, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
-    set_last_error("");
-    return W8A16_OK;
+    if (levers().log) {
+        snprintf(buf, sizeof buf,
+                 "w8a16: w8a16_act_quant_fp8 m=%u k=%u: per-token FP8 quantizer, one group of "
+                 "128 K elements per scale\n", m, k);
+        log_line(buf);
+    }
+    return launched(static_cast<hipStream_t>(stream));
 }
 
 int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float *a_scales,
@@ -377,7 +513,10 @@ int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float 
                             const w8a16_plan_t *plan, void *stream)
 {
     using namespace w8a16;
-    int st = check_call(qa, qa_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
+    int st = check_levers("w8a16_gemm_w8a8");
+    if (st != W8A16_OK)
+        return st;
+    st = check_call(qa, qa_row_stride, w_fp8, block_scale, c, c_row_stride, m, n, k);
     if (st != W8A16_OK)
         return st;
     if (qa_row_stride % 16 != 0) {
@@ -429,8 +568,9 @@ int w8a16_gemm_w8a8_planned(const void *qa, uint32_t qa_row_stride, const float 
     hipError_t e = launch_w8a8(g, a_scales, p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
-    set_last_error("");
-    return W8A16_OK;
+    log_plan(plan ? "w8a16_gemm_w8a8_planned" : "w8a16_gemm_w8a8", m, n, k, p,
+             plan ? nullptr : plan_reason());
+    return launched(static_cast<hipStream_t>(stream));
 }
 
 int w8a16_gemm_w8a8(const void *qa, uint32_t qa_row_stride, const float *a_scales,
@@ -447,7 +587,10 @@ int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t 
                             const w8a16_plan_t *plan, void *stream)
 {
     using namespace w8a16;
-    int st = check_args_w4a4(m, n, k, a_row_stride, c_row_stride);
+    int st = check_levers("w8a16_gemm_w4a4");
+    if (st != W8A16_OK)
+        return st;
+    st = check_args_w4a4(m, n, k, a_row_stride, c_row_stride);
     if (st != W8A16_OK)
         return st;
     if (!a || !a_scale || !w_fp4 || !w_scale || !c)
@@ -495,8 +638,9 @@ int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t 
     e = launch_w4a4(g, p, hs);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
-    set_last_error("");
-    return W8A16_OK;
+    log_plan(plan ? "w8a16_gemm_w4a4_planned" : "w8a16_gemm_w4a4", m, n, k, p,
+             plan ? nullptr : plan_reason());
+    return launched(hs);
 }
 
 int w8a16_gemm_w4a4(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
@@ -510,6 +654,8 @@ int w8a16_gemm_w4a4(const void *a, uint32_t a_row_stride, const uint8_t *a_scale
 int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *stream)
 {
     using namespace w8a16;
+    if (check_levers("w8a16_gemm_batched") != W8A16_OK)
+        return W8A16_ERR_ENV;
     if (!descs)
         return fail(W8A16_ERR_NULL_PTR, "w8a16_gemm_batched: null descriptors");
     if (count < 1 || count > W8A16_MAX_BATCH) {
@@ -567,8 +713,12 @@ int w8a16_gemm_batched(const w8a16_gemm_desc_t *descs, uint32_t count, void *str
     e = launch_stream_batched(b, plan, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
-    set_last_error("");
-    return W8A16_OK;
+    if (levers().log) {
+        char entry[64];
+        snprintf(entry, sizeof entry, "w8a16_gemm_batched (%u problems, the first)", count);
+        log_plan(entry, descs[0].m, descs[0].n, descs[0].k, plan, plan_reason());
+    }
+    return launched(static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@
 
 #include "plan.h"
 
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -25,7 +26,19 @@ namespace w8a16 {
 
 namespace {
 thread_local std::string g_last_error;
+thread_local char g_plan_reason[256];
+
+void set_reason(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+void set_reason(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_plan_reason, sizeof g_plan_reason, fmt, ap);
+    va_end(ap);
 }
+}  // namespace
+
+const char *plan_reason() { return g_plan_reason; }
 
 void set_last_error(const char *fmt_msg) { g_last_error = fmt_msg ? fmt_msg : ""; }
 
@@ -431,6 +444,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     StreamTile st16 = {1, 1, 0};
     if (m > 16)
         st16 = cheapest_stream_tile(m, nb16, p.cu_count);
+    const char *why = "";
     const bool stream_fits = m <= 128 && wbytes <= (16ull << 20) &&
                              (uint64_t)div_up(m, 16 * st16.mb) * div_up(nb16, st16.nb) <= p.cu_count;
     if (m > 128 || (m > 32 && wbytes > (16ull << 20)) || (m > 64 && !stream_fits)) {
@@ -443,6 +457,10 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.kernel = W8A16_KERNEL_TILE;
         p.flags = 0;
         p.m_blocks = m <= 128 ? 4 : 8;
+        why = m > 128 ? "m > 128: tile kernel, 128-row tiles"
+              : (m > 32 && wbytes > (16ull << 20))
+                  ? "m > 32 over a weight above 16 MiB: tile kernel, 64-row tiles"
+                  : "m > 64 and no stream tile fits one round per CU: tile kernel";
         const uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
         auto splits_fill = [&](uint32_t tiles) {
             uint32_t sp = 1;
@@ -479,6 +497,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         p.depth = 1;
         p.flags = 0;
         p.m_blocks = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+        why = "small m: stream kernel, widest column tile giving 3/4 of the CUs a tile";
         uint32_t m_tiles = div_up(m, 16 * p.m_blocks);
         const uint32_t fill = (3 * p.cu_count) / 4;
         uint32_t nbw = 1;
@@ -523,6 +542,8 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
             }
             m_tiles = div_up(m, 16 * p.m_blocks);
             by_cost = true;
+            why = "small m: stream kernel, the tile asking each CU for the fewest A and weight "
+                  "bytes";
         }
         p.n_blocks = nbw;
         const uint32_t pairs = p.m_blocks * p.n_blocks;
@@ -587,6 +608,7 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
                     p.depth = depth;
                     p.waves = rw;
                     chosen = true;
+                    why = "8..32 rows over a weight of 48 MiB or more: ring kernel";
                 }
             }
         }
@@ -594,6 +616,11 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
     st = plan_finalize(m, n, k, &p);
     if (st != W8A16_OK)
         return st;
+    if (p.splits > 1)
+        set_reason("%s; K split %u ways (%u tiles for %u CUs)", why, p.splits,
+                   p.m_tiles * p.n_tiles, p.cu_count);
+    else
+        set_reason("%s", why);
     *out = p;
     return W8A16_OK;
 }
@@ -672,6 +699,8 @@ int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
         p.m_blocks = ps_mb;
         p.n_blocks = 1;
         p.waves = ps_waves;
+        set_reason("W4A4: %u or more 16-row weight tiles per CU and A fits in LDS: "
+                   "persistent kernel", kW4a4PsMinTilesPerCu);
     } else {
         p.kernel = W8A16_KERNEL_W4A4;
         uint64_t best = ~0ull;
@@ -695,6 +724,7 @@ int make_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
         const uint32_t groups = div_up(ksteps, 4);
         while (p.waves > 4 && groups < 2 * p.waves)
             p.waves /= 2;
+        set_reason("W4A4: tiled kernel, the tile asking each CU for the fewest bytes");
     }
     st = plan_finalize(m, n, k, &p);
     if (st != W8A16_OK)
@@ -717,6 +747,7 @@ const char *status_string(int status)
     case W8A16_ERR_HIP: return "HIP runtime error";
     case W8A16_ERR_WORKSPACE: return "split-K workspace unavailable (growth during capture, "
                                      "or beyond the no-alloc scratch)";
+    case W8A16_ERR_ENV: return "W8A16_LOG or W8A16_DEBUG_SYNC is set to a value other than 0 or 1";
     default: return "unknown status";
     }
 }
@@ -790,6 +821,8 @@ int make_plan_w8a8(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_
     // Eight waves up to four blocks per tile (each keeps two K steps in
     // flight; sixteen measured 5 % slower at 8 x 4096 x 4096), else four.
     const uint32_t pairs = p.m_blocks * p.n_blocks;
+    set_reason("W8A8: widest column tile giving 3/4 of the CUs a tile%s",
+               m > 16 ? ", or the one asking each CU for the fewest bytes" : "");
     p.waves = pairs <= 4 ? 8 : 4;
     while (p.waves > 4 && (ksteps < 2 * p.waves ||
                            w8a8_lds_bytes(p.m_blocks, p.n_blocks, p.waves) > kMaxLdsBytes))
@@ -927,6 +960,7 @@ int plan_batched(const w8a16_gemm_desc_t *descs, uint32_t count, uint32_t cu_cou
     for (uint32_t i = 0; i < count; ++i)
         p.n_tiles += div_up(descs[i].n, 16 * p.n_blocks);
     p.steps_per_split = max_k / kKStep;
+    set_reason("batched: one stream-kernel tile for all %u problems, chosen for the tallest", count);
     *out = p;
     return W8A16_OK;
 }

@@ -171,6 +171,9 @@ int fail_with_name(int status, const char *name);
 // Prefix the last error with "w8a16_gemm_batched: descriptor <index>: ".
 int fail_at(int status, uint32_t index);
 const char *status_string(int status);
+// Why the calling thread's last successful default plan was chosen (the
+// planner rule that picked kernel and tile), for the plan log.
+const char *plan_reason();
 const char *last_error();
 void set_last_error(const char *msg);
 int fail(int status, const char *msg);

@@ -41,8 +41,8 @@
  * Errors: every entry point returns a w8a16_status.  Argument errors are
  * detected before anything is enqueued, in the order of the enum below
  * (codes 1..4 in the order the page checks them; 5..7 and 9 are checks the
- * page does not make).  w8a16_last_error() then holds a message for the calling
- * thread.  Launches are asynchronous: the call returns once the kernel is
+ * page does not make; 10, a bad diagnostic setting, is checked first).
+ * w8a16_last_error() then holds a message for the calling thread.  Launches are asynchronous: the call returns once the kernel is
  * enqueued on `stream`; a failed enqueue returns W8A16_ERR_HIP.
  */
 #ifndef W8A16_H
@@ -64,10 +64,27 @@ typedef enum w8a16_status {
     W8A16_ERR_NULL_PTR = 6,          /* a, w_fp8, block_scale or c is null */
     W8A16_ERR_BAD_PLAN = 7,          /* a plan that does not fit the problem */
     W8A16_ERR_HIP = 8,               /* allocation or launch failed in HIP */
-    W8A16_ERR_WORKSPACE = 9          /* the plan's split-K workspace cannot be provided:
+    W8A16_ERR_WORKSPACE = 9,         /* the plan's split-K workspace cannot be provided:
                                         it would have to grow during stream capture,
                                         or it exceeds w8a16_gemm_noalloc's scratch */
+    W8A16_ERR_ENV = 10               /* a diagnostic environment variable holds a value
+                                        other than 0 or 1 (see Diagnostics below) */
 } w8a16_status;
+
+/* Diagnostics.  Two environment variables, read once per process at the
+ * first call of an entry point that enqueues work (w8a16_gemm,
+ * _gemm_planned, _gemm_noalloc, _gemm_batched, _act_quant_fp8,
+ * _gemm_w8a8[_planned], _gemm_w4a4[_planned]); unset, empty or "0" is off,
+ * "1" is on, and any other value makes each of those calls return
+ * W8A16_ERR_ENV, before any other check, with the variable named in
+ * w8a16_last_error().  The pure planning calls ignore them.
+ *   W8A16_LOG=1: each distinct launch (entry point, m, n, k and plan) is
+ *     printed once to stderr: kernel, tile, K splits, waves, grid, LDS,
+ *     workspace, and for a default plan the planner rule that chose it.
+ *   W8A16_DEBUG_SYNC=1: after enqueuing, the call waits for the stream and
+ *     returns W8A16_ERR_HIP if the kernel failed.  On a stream being
+ *     captured into a graph it does not wait (nothing runs until replay).
+ *     It serialises the caller with the GPU: for debugging only. */
 
 /* Kernel families a plan can name. */
 typedef enum w8a16_kernel {
@@ -334,8 +351,9 @@ int w8a16_plan_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count,
 /* w8a16_gemm_w4a4 with an explicit plan (kernel W8A16_KERNEL_W4A4:
  * m_blocks 1, 2 or 4 and n_blocks 1, 2 or 4, not both 4, with 4 waves, 8
  * waves up to m_blocks + n_blocks = 4, 16 waves for 1 x 1; kernel
- * W8A16_KERNEL_W4A4_PS: m_blocks 1 or 2 covering m, waves 8 or 16).  For
- * tests and tuning. */
+ * W8A16_KERNEL_W4A4_PS: m_blocks 1, 2 or 4 covering m, 4, 8 or 16 waves,
+ * and the staged activations plus two partial tiles per wave within the
+ * LDS, else W8A16_ERR_BAD_PLAN).  For tests and tuning. */
 int w8a16_gemm_w4a4_planned(const void *a, uint32_t a_row_stride, const uint8_t *a_scale,
                             const void *w_fp4, const uint8_t *w_scale, void *c,
                             uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k,

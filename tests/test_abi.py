@@ -656,3 +656,22 @@ def test_w4a4_plan_errors():
     # A and the partial tiles must fit in LDS: 64 rows x 4096 K at 16 waves do not
     with pytest.raises(w8.W8A16Error):
         w8.make_plan(64, 4096, 4096, w8.KERNEL_W4A4_PS, 4, 1, 1, waves=16)
+
+
+def test_torch_bindings_reject_host_tensors():
+    """The tensor-level entry points refuse host tensors before any library
+    call (a host pointer handed to a kernel would fault the GPU)."""
+    import torch
+    a = torch.zeros((4, 256), dtype=torch.bfloat16)
+    w = torch.zeros((64, 256), dtype=torch.uint8)
+    s = torch.ones((1, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        w8.gemm(a, w, s)
+    qa = torch.zeros((4, 256), dtype=torch.uint8)
+    sa = torch.ones((4, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        w8.gemm_w8a8(qa, sa, w, s)
+    with pytest.raises(ValueError, match="a_scales must hold"):
+        w8.gemm_w8a8(qa, sa[:2], w, s)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        w8.act_quant_fp8(a)
