@@ -485,6 +485,27 @@ int make_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t cu_count, w8a16_plan_
         }
         if (p.splits < div_up(ksteps, kTileMaxSteps))
             p.splits = div_up(ksteps, kTileMaxSteps);
+        // 65..128 rows: one 128 x 128 tile per column block, so the weight
+        // crosses HBM once, when the K splits that fill the CUs keep 16 or
+        // more K steps each (measured on MI355X, us per call, two 64-row
+        // tiles -> one 128-row tile with 4 splits: 128 x 8192 x 8192
+        // 32.1-32.9 -> 31.1-31.3, 96 x 8192 x 8192 31.3-31.6 -> 30.6-30.8,
+        // 72 x 8192 x 8192 30.5-30.7 -> 29.4-30.1; with 8 steps per split
+        // it is even at 128 x 8192 x 4096 and loses at 128 x 4096 x 8192,
+        // 21.5-22.0 -> 25.2-26.2).
+        if (m > 64 && m <= 128) {
+            const uint32_t sp = splits_fill(div_up(n, 128));
+            if (ksteps / sp >= 16 && sp >= div_up(ksteps, kTileMaxSteps)) {
+                p.m_blocks = 8;
+                p.n_blocks = 8;
+                p.splits = sp;
+                p.depth = 3;
+                p.a_depth = 3;
+                p.waves = 8;
+                why = "65..128 rows with K splits of 16 or more steps: tile kernel, one 128-row "
+                      "tile (the weight read once)";
+            }
+        }
     } else {
         // Small m: the weight-streaming kernel.  Measured on MI355X, the
         // best plans give each CU about one workgroup tile, enough waves

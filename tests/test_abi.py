@@ -172,12 +172,20 @@ def test_ring_plans():
 def test_large_m_plans_tile_kernel():
     p = w8.plan(128, 8192, 8192)
     assert p.kernel == w8.KERNEL_TILE
-    # two 64-row tiles x 64 128-column tiles x 2 splits: one workgroup per CU
-    assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (4, 8, 2, 32)
-    assert (p.m_tiles, p.grid, p.counter_count) == (2, 256, 0)
-    assert p.workspace_bytes == 2 * 128 * 8192 * 4
-    assert p.lds_bytes == p.a_depth * 64 * 256 + p.depth * 128 * 128 + 256
+    # one 128-row tile x 64 128-column tiles x 4 splits of 16 K steps: one
+    # workgroup per CU, the weight read once
+    assert (p.m_blocks, p.n_blocks, p.splits, p.steps_per_split) == (8, 8, 4, 16)
+    assert (p.depth, p.a_depth, p.waves) == (3, 3, 8)
+    assert (p.m_tiles, p.grid, p.counter_count) == (1, 256, 0)
+    assert p.workspace_bytes == 4 * 128 * 8192 * 4
+    assert p.lds_bytes == p.a_depth * 128 * 256 + p.depth * 128 * 128 + 256
     assert p.lds_bytes <= 160 * 1024 - 256
+    assert (w8.plan(65, 8192, 8192).m_blocks, w8.plan(96, 8192, 8192).m_blocks) == (8, 8)
+    # splits of 8 K steps keep two 64-row tiles
+    for n, k in ((8192, 4096), (4096, 8192)):
+        p = w8.plan(128, n, k)
+        assert (p.kernel, p.m_blocks, p.n_blocks, p.m_tiles) == (w8.KERNEL_TILE, 4, 8, 2), (n, k)
+        assert p.grid == 256 and p.lds_bytes == p.a_depth * 64 * 256 + p.depth * 128 * 128 + 256
     p3 = w8.make_plan(128, 8192, 8192, w8.KERNEL_TILE, 8, 8, 4, depth=3, a_depth=3,
                       waves=4)
     assert p3.lds_bytes == 3 * 128 * 256 + 3 * 128 * 128 + 256
