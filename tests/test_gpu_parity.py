@@ -863,6 +863,58 @@ def test_w8a8_default_plan_within_tolerance(w8, m, n, k):
     assert oracle.within_tolerance(c[rows, cols], oc, bound).all()
 
 
+def test_graph_replays_quantizer_w8a8_and_batched(w8):
+    """The FP8 quantizer, the W8A8 GEMM it feeds and a batched call,
+    captured in one HIP graph, replayed three times with eager work and
+    synchronisations between the replays: every replay equals the eager
+    results bit for bit (outputs cleared before each replay)."""
+    m, n, k = 16, 2048, 1024
+    p = datagen.make_problem(m, n, k, seed=77)
+    a, ww, sw = dev_u16(p.a), dev(p.w), dev(p.scale)
+    q = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((m, k // 128), dtype=torch.float32, device="cuda")
+    c8 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    arms = [datagen.make_problem(8, nn, 512, seed=78 + nn) for nn in (512, 256)]
+    abufs = [(dev_u16(x.a), dev(x.w), dev(x.scale), dev_u16(x.c)) for x in arms]
+    descs = [dict(a=t[0].data_ptr(), w_fp8=t[1].data_ptr(), block_scale=t[2].data_ptr(),
+                  c=t[3].data_ptr(), a_row_stride=x.a_row_stride, c_row_stride=x.c_row_stride,
+                  m=x.m, n=x.n, k=x.k) for x, t in zip(arms, abufs)]
+    stream = torch.cuda.Stream()
+
+    def work():
+        assert w8.act_quant_fp8_raw(a.data_ptr(), k, q.data_ptr(), k, sa.data_ptr(), m, k,
+                                    stream.cuda_stream) == 0, w8.last_error()
+        assert w8.gemm_w8a8_raw(q.data_ptr(), k, sa.data_ptr(), ww.data_ptr(), sw.data_ptr(),
+                                c8.data_ptr(), n, m, n, k, stream.cuda_stream) == 0, \
+            w8.last_error()
+        assert w8.gemm_batched_raw(descs, stream.cuda_stream) == 0, w8.last_error()
+
+    def outputs():
+        return [t.clone() for t in (q, sa, c8)] + [t[3].clone() for t in abufs]
+
+    with torch.cuda.stream(stream):
+        work()
+        torch.cuda.synchronize()
+        eager = outputs()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            work()
+        for rep in range(3):
+            for t in [q, sa, c8] + [t[3] for t in abufs]:
+                t.zero_()
+            work()                              # eager work between replays
+            torch.cuda.synchronize()
+            for t in [q, sa, c8] + [t[3] for t in abufs]:
+                t.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for want, got in zip(eager, outputs()):
+                assert torch.equal(want, got), "replay %d differs from eager" % rep
+    oq, os_ = oracle.act_quant(p.a, m, k)
+    assert np.array_equal(eager[0].cpu().numpy(), oq)
+
+
 def test_quantize_then_w8a8_pipeline(w8):
     """BF16 activations -> GPU quantizer -> GPU W8A8 GEMM, against the
     oracle's quantizer and W8A8 GEMM: identical codes and scales, outputs
