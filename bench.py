@@ -998,6 +998,9 @@ def main():
                    "us_per_call_warm: the same on one set of buffers, after the cold timing "
                    "(the weight may stay in the Infinity Cache), context only"),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "peaks": {"hbm_gbs": HBM_PEAK_GBS, "bf16_dense_tflops": BF16_PEAK_TFLOPS,
+                  "source": "published MI355X figures (HBM3E 8 TB/s; dense BF16 MFMA "
+                            "2.5 PFLOP/s), the denominators of pct_hbm and pct_mfma"},
         "tflops": round(wl.flops() / (ms_call * 1e-3) / 1e12, 3),
         "plan": plan.as_dict(),
         "output_sane": sane,
