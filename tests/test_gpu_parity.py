@@ -283,6 +283,41 @@ def test_default_split_plans_at_size_sampled(w8, m, n, k):
         assert (g[m:, :] == p.c[m:, :]).all()
 
 
+@pytest.mark.parametrize("m,n,k", [(3, 34816, 131072), (128, 36864, 131072)])
+def test_weight_above_4_gib_sampled(w8, m, n, k):
+    """A weight of more than 4 GiB under the default plan (a stream plan and
+    a tile plan with 16 K splits): W's code in row j, K block b is
+    0x30 + j % 7 + b % 5, so a row or K offset that wraps at 2^32 bytes
+    (rows 32768 apart differ in j % 7) reads other values; sampled outputs,
+    including the last rows and those just past 2^32 bytes, against the
+    oracle, and C's extra row untouched."""
+    rng = np.random.default_rng(4242 + m)
+    w = np.empty((n, k), dtype=np.uint8)
+    np.add((0x30 + np.arange(n) % 7).astype(np.uint8)[:, None],
+           np.repeat((np.arange(k // 128) % 5).astype(np.uint8), 128)[None, :], out=w)
+    assert w.nbytes > 1 << 32
+    scale = rng.uniform(0.5, 2.0, size=(-(-n // 128), k // 128)).astype(np.float32)
+    a = datagen.to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    c = np.full((m + 1, n), datagen.C_SENTINEL, dtype=np.uint16)
+    print("weight above 4 GiB: m=%d n=%d k=%d plan=%s" % (m, n, k, w8.plan(m, n, k).as_dict()),
+          flush=True)
+    ad, wd, sd, cd = dev_u16(a), dev(w), dev(scale), dev_u16(c)
+    st = w8.gemm_raw(ad.data_ptr(), k, wd.data_ptr(), sd.data_ptr(), cd.data_ptr(), n, m, n, k)
+    assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    g = cd.cpu().numpy().view(np.uint16).reshape(c.shape)
+    del ad, wd, sd, cd
+    torch.cuda.empty_cache()
+    rows, cols = datagen.sample_indices(m, n, 300, seed=11)
+    wrap = (1 << 32) // k                      # first weight row past 2^32 bytes
+    extra_c = np.array([n - 1, n - 2, wrap - 1, wrap, wrap + 1], dtype=np.uint32)
+    rows = np.concatenate([rows, np.repeat(np.uint32(m - 1), 5), np.zeros(5, np.uint32)])
+    cols = np.concatenate([cols, extra_c, extra_c])
+    oc, _, bound = oracle.gemm_at(a, w, scale, m, n, k, rows, cols)
+    assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+    assert (g[m, :] == datagen.C_SENTINEL).all()
+
+
 RING_SHAPES = [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)]
 
 
