@@ -283,18 +283,34 @@ def test_default_split_plans_at_size_sampled(w8, m, n, k):
         assert (g[m:, :] == p.c[m:, :]).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(3, 34816, 131072), (128, 36864, 131072)])
+def _big_weight(n, k):
+    """[n, k] E4M3 codes 0x30 + j % 7 + b % 5 for row j, K block b: rows
+    32768 apart and neighbouring K blocks hold different values."""
+    w = np.empty((n, k), dtype=np.uint8)
+    np.add((0x30 + np.arange(n) % 7).astype(np.uint8)[:, None],
+           np.repeat((np.arange(k // 128) % 5).astype(np.uint8), 128)[None, :], out=w)
+    return w
+
+
+def _big_samples(m, n, k):
+    rows, cols = datagen.sample_indices(m, n, 300, seed=11)
+    wrap = (1 << 32) // k                      # first weight row past 2^32 bytes
+    extra_c = np.array([n - 1, n - 2, wrap - 1, wrap, wrap + 1], dtype=np.uint32)
+    rows = np.concatenate([rows, np.repeat(np.uint32(m - 1), 5), np.zeros(5, np.uint32)])
+    return rows, np.concatenate([cols, extra_c, extra_c])
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 34816, 131072), (24, 36864, 131072),
+                                   (128, 36864, 131072)])
 def test_weight_above_4_gib_sampled(w8, m, n, k):
-    """A weight of more than 4 GiB under the default plan (a stream plan and
-    a tile plan with 16 K splits): W's code in row j, K block b is
+    """A weight of more than 4 GiB under the default plan (a stream plan, a
+    ring plan and a tile plan with 16 K splits): W's code in row j, K block b is
     0x30 + j % 7 + b % 5, so a row or K offset that wraps at 2^32 bytes
     (rows 32768 apart differ in j % 7) reads other values; sampled outputs,
     including the last rows and those just past 2^32 bytes, against the
     oracle, and C's extra row untouched."""
     rng = np.random.default_rng(4242 + m)
-    w = np.empty((n, k), dtype=np.uint8)
-    np.add((0x30 + np.arange(n) % 7).astype(np.uint8)[:, None],
-           np.repeat((np.arange(k // 128) % 5).astype(np.uint8), 128)[None, :], out=w)
+    w = _big_weight(n, k)
     assert w.nbytes > 1 << 32
     scale = rng.uniform(0.5, 2.0, size=(-(-n // 128), k // 128)).astype(np.float32)
     a = datagen.to_bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
@@ -308,11 +324,7 @@ def test_weight_above_4_gib_sampled(w8, m, n, k):
     g = cd.cpu().numpy().view(np.uint16).reshape(c.shape)
     del ad, wd, sd, cd
     torch.cuda.empty_cache()
-    rows, cols = datagen.sample_indices(m, n, 300, seed=11)
-    wrap = (1 << 32) // k                      # first weight row past 2^32 bytes
-    extra_c = np.array([n - 1, n - 2, wrap - 1, wrap, wrap + 1], dtype=np.uint32)
-    rows = np.concatenate([rows, np.repeat(np.uint32(m - 1), 5), np.zeros(5, np.uint32)])
-    cols = np.concatenate([cols, extra_c, extra_c])
+    rows, cols = _big_samples(m, n, k)
     oc, _, bound = oracle.gemm_at(a, w, scale, m, n, k, rows, cols)
     assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
     assert (g[m, :] == datagen.C_SENTINEL).all()
@@ -896,6 +908,26 @@ def test_w8a8_default_plan_within_tolerance(w8, m, n, k):
     rows, cols = datagen.sample_indices(m, n, 2000, seed=9)
     oc, _, bound = oracle.gemm_w8a8_at(qa, sa, w, sw, m, n, k, rows, cols)
     assert oracle.within_tolerance(c[rows, cols], oc, bound).all()
+
+
+def test_w8a8_weight_above_4_gib_sampled(w8):
+    """The W8A8 GEMM over a weight of more than 4 GiB (default plan): codes
+    as in the W8A16 case, random finite FP8 activations and scales; sampled
+    outputs, including rows past 2^32 bytes, against the oracle."""
+    m, n, k = 16, 34816, 131072
+    rng = np.random.default_rng(4343)
+    w = _big_weight(n, k)
+    qa = (rng.integers(0, 0x7F, size=(m, k), dtype=np.uint8) |
+          (rng.integers(0, 2, size=(m, k), dtype=np.uint8) << 7))
+    sa = rng.uniform(0.01, 0.1, size=(m, k // 128)).astype(np.float32)
+    sw = rng.uniform(0.5, 2.0, size=(-(-n // 128), k // 128)).astype(np.float32)
+    print("W8A8 weight above 4 GiB: plan=%s" % w8.plan_w8a8(m, n, k).as_dict(), flush=True)
+    c = run_w8a8(w8, qa, sa, w, sw, m, n, k, k, n, m + 1)
+    torch.cuda.empty_cache()
+    rows, cols = _big_samples(m, n, k)
+    oc, _, bound = oracle.gemm_w8a8_at(qa, sa, w, sw, m, n, k, rows, cols)
+    assert oracle.within_tolerance(c[rows, cols], oc, bound).all()
+    assert (c[m, :] == 0x7777).all()
 
 
 def test_graph_replays_quantizer_w8a8_and_batched(w8):
