@@ -108,6 +108,9 @@ def _load():
         lib.oracle_w4a4_gemm.argtypes = [u8p, u32, u8p, u8p, u8p, u16p, u32, u32, u32, u32,
                                          f64p, f64p, ctypes.c_int]
         lib.oracle_w4a4_gemm.restype = ctypes.c_int
+        lib.oracle_w4a4_gemm_at.argtypes = [u8p, u32, u8p, u8p, u8p, u32, u32, u32, u32p, u32p,
+                                            ctypes.c_int64, u16p, f64p, f64p, ctypes.c_int]
+        lib.oracle_w4a4_gemm_at.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -345,6 +348,35 @@ def gemm_w4a4(a: np.ndarray, a_scale: np.ndarray, w: np.ndarray, w_scale: np.nda
         int(threads))
     if rc != 0:
         raise ValueError("oracle: invalid W4A4 shape m=%d n=%d k=%d" % (m, n, k))
+    return c, tot, bound
+
+
+def gemm_w4a4_at(a: np.ndarray, a_scale: np.ndarray, w: np.ndarray, w_scale: np.ndarray,
+                 m: int, n: int, k: int, rows: np.ndarray, cols: np.ndarray,
+                 a_row_stride: Optional[int] = None, threads: int = 0
+                 ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Selected W4A4 outputs C[rows[s], cols[s]] (operands as for
+    gemm_w4a4): (c_bits uint16 [s], tot float64 [s], bound float64 [s])."""
+    a_row_stride = k if a_row_stride is None else int(a_row_stride)
+    a = np.ascontiguousarray(a, dtype=np.uint8).reshape(-1)
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.uint8).reshape(-1)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.uint8).reshape(-1)
+    assert a.size >= (m - 1) * (a_row_stride // 2) + k // 2 and w.size >= n * k // 2
+    assert a_scale.size >= m * (k // MX_BLOCK) and w_scale.size >= n * (k // MX_BLOCK)
+    rows = np.ascontiguousarray(rows, dtype=np.uint32).reshape(-1)
+    cols = np.ascontiguousarray(cols, dtype=np.uint32).reshape(-1)
+    ns = rows.size
+    c = np.zeros(ns, dtype=np.uint16)
+    tot = np.empty(ns, dtype=np.float64)
+    bound = np.empty(ns, dtype=np.float64)
+    rc = _load().oracle_w4a4_gemm_at(
+        _ptr(a, ctypes.c_uint8), a_row_stride, _ptr(a_scale, ctypes.c_uint8),
+        _ptr(w, ctypes.c_uint8), _ptr(w_scale, ctypes.c_uint8), m, n, k,
+        _ptr(rows, ctypes.c_uint32), _ptr(cols, ctypes.c_uint32), ns, _ptr(c, ctypes.c_uint16),
+        _ptr(tot, ctypes.c_double), _ptr(bound, ctypes.c_double), int(threads))
+    if rc != 0:
+        raise ValueError("oracle: invalid W4A4 shape or sample index")
     return c, tot, bound
 
 

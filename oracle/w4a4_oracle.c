@@ -123,3 +123,43 @@ int oracle_w4a4_gemm(const uint8_t *a, uint32_t a_row_stride, const uint8_t *a_s
 #endif
     return 0;
 }
+
+/* Selected outputs only, for shapes too large to compute whole: sample s is
+ * C[rows[s]][cols[s]], operands as for oracle_w4a4_gemm.  c_out receives
+ * BF16 bits, tot and bound doubles (each may be null).  Returns -1 for a
+ * shape it does not take or an index out of range (before reading any
+ * operand). */
+int oracle_w4a4_gemm_at(const uint8_t *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                        const uint8_t *w, const uint8_t *w_scale, uint32_t m, uint32_t n,
+                        uint32_t k, const uint32_t *rows, const uint32_t *cols, int64_t nsamp,
+                        uint16_t *c_out, double *tot, double *bound, int nthreads)
+{
+    if (m == 0 || n == 0 || k == 0 || k % W4A4_BLOCK != 0 || a_row_stride < k ||
+        a_row_stride % 2u != 0 || nsamp < 0)
+        return -1;
+    for (int64_t s = 0; s < nsamp; ++s)
+        if (rows[s] >= m || cols[s] >= n)
+            return -1;
+    const uint32_t kb = k / W4A4_BLOCK;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t s = 0; s < nsamp; ++s) {
+        const uint32_t i = rows[s], j = cols[s];
+        double t, b;
+        w4a4_one(a + (size_t)i * (a_row_stride / 2u), a_scale + (size_t)i * kb,
+                 w + (size_t)j * (k / 2u), w_scale + (size_t)j * kb, k, &t, &b);
+        if (c_out)
+            c_out[s] = oracle_bf16_rne(t);
+        if (tot)
+            tot[s] = t;
+        if (bound)
+            bound[s] = b;
+    }
+#ifndef _OPENMP
+    (void)nthreads;
+#endif
+    return 0;
+}

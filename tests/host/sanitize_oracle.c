@@ -41,6 +41,10 @@ int oracle_w4a4_gemm(const uint8_t *a, uint32_t a_row_stride, const uint8_t *a_s
                      const uint8_t *w, const uint8_t *w_scale, uint16_t *c,
                      uint32_t c_row_stride, uint32_t m, uint32_t n, uint32_t k, double *tot,
                      double *bound, int nthreads);
+int oracle_w4a4_gemm_at(const uint8_t *a, uint32_t a_row_stride, const uint8_t *a_scale,
+                        const uint8_t *w, const uint8_t *w_scale, uint32_t m, uint32_t n,
+                        uint32_t k, const uint32_t *rows, const uint32_t *cols, int64_t nsamp,
+                        uint16_t *c_out, double *tot, double *bound, int nthreads);
 
 static uint64_t g_state = 0x13198a2e03707344ull;
 
@@ -157,6 +161,14 @@ static void run_w4a4(uint32_t m, uint32_t n, uint32_t k, uint32_t pad_a, uint32_
     expect_status(oracle_w4a4_gemm(a, as, sa, w, sw, c, cs, m, n, k, tot, bnd, 1), 0, "w4a4");
     expect_status(oracle_w4a4_gemm(a, as, sa, w, sw, c, cs, m, n, k, NULL, NULL, 1), 0,
                   "w4a4 without diagnostics");
+    uint32_t rows[3] = {m - 1, 0, m / 2}, cols[3] = {0, n - 1, n / 2};
+    uint16_t co[3];
+    double t3[3], b3[3];
+    expect_status(oracle_w4a4_gemm_at(a, as, sa, w, sw, m, n, k, rows, cols, 3, co, t3, b3, 1),
+                  0, "w4a4 sampled");
+    cols[1] = n;  /* out of range: rejected before any read */
+    expect_status(oracle_w4a4_gemm_at(a, as, sa, w, sw, m, n, k, rows, cols, 3, co, t3, b3, 1),
+                  -1, "w4a4 sampled, column out of range");
     free(a);
     free(sa);
     free(w);

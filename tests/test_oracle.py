@@ -746,6 +746,29 @@ def test_w4a4_gemm_equals_exact_rational_then_rne(m, n, k, pad):
             assert tot[i, j] == float(exact[i, j])
 
 
+def test_w4a4_gemm_at_equals_exact_rational_then_rne():
+    """The sampled W4A4 entry: selected outputs (repeats and any order)
+    against brute force with exact rationals, and every index checked
+    before any read."""
+    rng = np.random.default_rng(733)
+    m, n, k, pad = 3, 7, 128, 64
+    a, asc, w, wsc = _mx_rand(rng, m, n, k, k + pad)
+    exact = _exact_w4a4(a, asc, w, wsc, m, n, k)
+    rows = np.array([2, 0, 1, 2, 2, 0], np.uint32)
+    cols = np.array([6, 0, 3, 6, 1, 5], np.uint32)
+    c, tot, bound = oracle.gemm_w4a4_at(a, asc, w, wsc, m, n, k, rows, cols,
+                                        a_row_stride=k + pad)
+    for s_, (i, j) in enumerate(zip(rows, cols)):
+        assert int(c[s_]) == brute_bf16_rne(exact[i, j]), (i, j)
+        assert tot[s_] == float(exact[i, j])
+    _, _, full_bound = oracle.gemm_w4a4(a, asc, w, wsc, m, n, k, a_row_stride=k + pad)
+    assert np.array_equal(bound, full_bound[rows, cols])
+    for bad_r, bad_c in [(m, 0), (0, n)]:
+        with pytest.raises(ValueError):
+            oracle.gemm_w4a4_at(a, asc, w, wsc, m, n, k, np.array([bad_r], np.uint32),
+                                np.array([bad_c], np.uint32), a_row_stride=k + pad)
+
+
 def test_w4a4_pad_is_not_read():
     rng = np.random.default_rng(11)
     a, asc, w, wsc = _mx_rand(rng, 2, 4, 128, 192)

@@ -189,6 +189,43 @@ def test_w4a4_determinism_and_graph_replay(w8):
             assert np.array_equal(c.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("m,n,k", [(8, 69632, 131072), (16, 540672, 16384)])
+def test_w4a4_weight_above_4_gib_sampled(w8, m, n, k):
+    """A packed FP4 weight of more than 4 GiB under the default plan (tiled,
+    then persistent): row j holds E2M1 code 1 + j % 7 in both nibbles and
+    its K blocks' scales cycle through 2^-1, 2^0, 2^1, so a row or K offset
+    that wraps at 2^32 bytes reads other values; sampled outputs, including
+    the rows just past 2^32 bytes and the last rows, against the oracle."""
+    rng = np.random.default_rng(4444 + m)
+    code = (1 + np.arange(n) % 7).astype(np.uint8)
+    w = np.empty((n, k // 2), dtype=np.uint8)
+    w[:] = (code | (code << 4))[:, None]
+    assert w.nbytes > 1 << 32
+    wsc = np.empty((n, k // 32), dtype=np.uint8)
+    wsc[:] = (126 + np.arange(k // 32) % 3).astype(np.uint8)[None, :]
+    a = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    asc = rng.integers(125, 130, size=(m, k // 32), dtype=np.uint8)
+    print("W4A4 weight above 4 GiB: m=%d n=%d k=%d plan=%s"
+          % (m, n, k, w8.plan_w4a4(m, n, k).as_dict()), flush=True)
+    ad, ascd, wd, wscd = _dev(a), _dev(asc), _dev(w), _dev(wsc)
+    c = torch.full((m + 1, n), 0x7777, dtype=torch.int16, device="cuda")
+    st = w8.gemm_w4a4_raw(ad.data_ptr(), k, ascd.data_ptr(), wd.data_ptr(), wscd.data_ptr(),
+                          c.data_ptr(), n, m, n, k)
+    assert st == 0, w8.last_error()
+    torch.cuda.synchronize()
+    g = c.cpu().numpy().view(np.uint16)
+    del ad, ascd, wd, wscd, c
+    torch.cuda.empty_cache()
+    rows, cols = datagen.sample_indices(m, n, 300, seed=12)
+    wrap = (1 << 32) // (k // 2)               # first weight row past 2^32 bytes
+    extra = np.array([n - 1, n - 2, wrap - 1, wrap, wrap + 1], dtype=np.uint32)
+    rows = np.concatenate([rows, np.repeat(np.uint32(m - 1), 5), np.zeros(5, np.uint32)])
+    cols = np.concatenate([cols, extra, extra])
+    oc, _, bound = oracle.gemm_w4a4_at(a, asc, w, wsc, m, n, k, rows, cols)
+    assert oracle.within_tolerance(g[rows, cols], oc, bound).all()
+    assert (g[m, :] == 0x7777).all()
+
+
 def test_w4a4_argument_errors_leave_c_untouched(w8):
     m, n, k = 8, 256, 512
     p = datagen.make_mx_problem(m, n, k, seed=5)
